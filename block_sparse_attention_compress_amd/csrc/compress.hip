@@ -1,0 +1,98 @@
+// a1 -- block keys: the fp32 mean of each 4-token microblock's keys.
+//
+// The QSA indexer compresses keys into microblocks of 4 tokens ("Qwen 4 QSA
+// krijgt decode-contextparallellisme", section "Wat de pull request
+// daadwerkelijk verandert").  How a block key is pooled is not stated; the
+// library uses the fp32 mean with a fixed add order, ((k0+k1)+(k2+k3))*0.25 for
+// a full block and (left-to-right sum) / n for a partial last block, so that the
+// result is reproducible bit for bit.
+//
+// One workgroup per (64-token chunk, KV head, sequence); chunks start at the
+// one holding first_token, so a decode refresh launches one chunk per
+// (sequence, KV head).  Thread t handles
+// microblock t/16 of the chunk and dims 16*(t%16) .. +15: four 32-byte key reads,
+// one 64-byte block-key write.  A pure HBM stream (read 2 B, write 1 B per key
+// element of a block).
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace qsa {
+
+__global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restrict__ k, float* __restrict__ ckey,
+                                                       const int32_t* __restrict__ block_table,
+                                                       const int32_t* __restrict__ seq_lens,
+                                                       const int32_t* __restrict__ first_token, int Hkv, int lg_ps,
+                                                       int max_pages) {
+    const int seq = blockIdx.z;
+    const int h = blockIdx.y;
+    const int L = seq_lens[seq];
+    const int first = first_token ? max(first_token[seq], 0) : 0;
+    const int mb = threadIdx.x >> 4;
+    const int e = threadIdx.x & 15;
+    // chunks are counted from the one holding first_token
+    const int64_t chunk = (int64_t)(first >> 6) + blockIdx.x;
+    const int64_t pos0 = (chunk * 16 + mb) * 4;
+    if (pos0 >= L || pos0 + 3 < first) return;
+    const int n = (L - pos0) < 4 ? (int)(L - pos0) : 4;
+
+    const int64_t row = token_row(block_table, seq, max_pages, Hkv, h, lg_ps, pos0);
+    const uint4* src = reinterpret_cast<const uint4*>(k + row * kHeadDim + 16 * e);
+    // the 4 tokens of a block are consecutive rows of one page (page_size is a
+    // power of two >= 4): token u is 256 elements = 32 uint4 further on
+    uint4 a[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (u < n) {
+            a[u][0] = src[u * 32];
+            a[u][1] = src[u * 32 + 1];
+        } else {
+            a[u][0] = make_uint4(0, 0, 0, 0);
+            a[u][1] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    float r[16];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const uint32_t w0 = (&a[0][w >> 2].x)[w & 3];
+        const uint32_t w1 = (&a[1][w >> 2].x)[w & 3];
+        const uint32_t w2 = (&a[2][w >> 2].x)[w & 3];
+        const uint32_t w3 = (&a[3][w >> 2].x)[w & 3];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const float k0 = half ? bf16_hi(w0) : bf16_lo(w0);
+            const float k1 = half ? bf16_hi(w1) : bf16_lo(w1);
+            const float k2 = half ? bf16_hi(w2) : bf16_lo(w2);
+            const float k3 = half ? bf16_hi(w3) : bf16_lo(w3);
+            float v;
+            if (n == 4) {
+                const float s01 = k0 + k1;
+                const float s23 = k2 + k3;
+                v = (s01 + s23) * 0.25f;
+            } else if (n == 3) {
+                v = __fdiv_rn((k0 + k1) + k2, 3.0f);
+            } else if (n == 2) {
+                v = (k0 + k1) * 0.5f;  // exact halving == division by 2
+            } else {
+                v = k0;
+            }
+            r[2 * w + half] = v;
+        }
+    }
+    // block-key row in [num_pages][Hkv][page_size / 4][256]
+    const int64_t brow = ((row >> lg_ps) << (lg_ps - 2)) + ((row & ((1 << lg_ps) - 1)) >> 2);
+    float4* dst = reinterpret_cast<float4*>(ckey + brow * kHeadDim + 16 * e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_float4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
+}
+
+hipError_t launch_compress(const PagedKV& kv, const int32_t* first_token, int span, hipStream_t st) {
+    if (kv.batch == 0 || kv.max_seq_len == 0) return hipSuccess;
+    // tokens [first, first + span) touch at most ceil(span / 64) + 1 chunks
+    const int chunks = first_token ? (span + 63) / 64 + 1 : (kv.max_seq_len + 63) / 64;
+    dim3 grid(chunks, kv.Hkv, kv.batch);
+    hipLaunchKernelGGL(compress_kernel, grid, dim3(256), 0, st, kv.k, kv.ckey, kv.block_table, kv.seq_lens,
+                       first_token, kv.Hkv, kv.lg_ps, kv.max_pages);
+    return hipGetLastError();
+}
+
+}  // namespace qsa

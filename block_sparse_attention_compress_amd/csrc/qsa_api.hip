@@ -1,0 +1,263 @@
+// C ABI of libqsa.so: host-side validation, then kernel launches.  Nothing here
+// touches HIP before the arguments have been accepted, so a rejected call costs
+// no device work and can be tested without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "qsa.h"
+#include "qsa_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return QSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int log2_exact(int v) {
+    if (v <= 0 || (v & (v - 1))) return -1;
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+// Checks the cache descriptor.  need_kv: K and V are read; need_ckey: block
+// keys are read or written.
+int check_kv(const qsa_kv_t* kv, bool need_k, bool need_v, bool need_ckey, qsa::PagedKV* out) {
+    if (!kv) return fail(QSA_ERR_INVALID_ARG, "kv descriptor is NULL");
+    if (need_k && !kv->k) return fail(QSA_ERR_INVALID_ARG, "kv->k is NULL");
+    if (need_v && !kv->v) return fail(QSA_ERR_INVALID_ARG, "kv->v is NULL");
+    if (need_ckey && !kv->ckey) return fail(QSA_ERR_INVALID_ARG, "kv->ckey is NULL");
+    if (!kv->block_table || !kv->seq_lens) return fail(QSA_ERR_INVALID_ARG, "kv->block_table / seq_lens is NULL");
+    if ((need_k && !aligned(kv->k, 16)) || (need_v && !aligned(kv->v, 16)) || (need_ckey && !aligned(kv->ckey, 16)))
+        return fail(QSA_ERR_INVALID_ARG, "k, v and ckey must be 16-byte aligned");
+    if (kv->head_dim != QSA_HEAD_DIM)
+        return fail(QSA_ERR_UNSUPPORTED, "head_dim %d: only %d is supported", kv->head_dim, QSA_HEAD_DIM);
+    if (kv->batch < 0 || kv->batch > 65535) return fail(QSA_ERR_INVALID_ARG, "batch %d out of [0, 65535]", kv->batch);
+    if (kv->num_kv_heads < 1 || kv->num_kv_heads > 65535)
+        return fail(QSA_ERR_INVALID_ARG, "num_kv_heads %d out of [1, 65535]", kv->num_kv_heads);
+    const int lg = log2_exact(kv->page_size);
+    if (lg < 2) return fail(QSA_ERR_INVALID_ARG, "page_size %d is not a power of two >= 4", kv->page_size);
+    if (kv->num_pages < 1 || kv->max_pages_per_seq < 1)
+        return fail(QSA_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be >= 1");
+    if (kv->max_seq_len < 0) return fail(QSA_ERR_INVALID_ARG, "max_seq_len %d < 0", kv->max_seq_len);
+    if (kv->max_seq_len > QSA_MAX_SEQ_LEN)
+        return fail(QSA_ERR_UNSUPPORTED, "max_seq_len %d exceeds %d", kv->max_seq_len, QSA_MAX_SEQ_LEN);
+    if ((int64_t)kv->max_pages_per_seq * kv->page_size < kv->max_seq_len)
+        return fail(QSA_ERR_INVALID_ARG, "max_pages_per_seq * page_size < max_seq_len");
+    if ((int64_t)kv->num_pages * kv->num_kv_heads * kv->page_size >= (int64_t)1 << 31)
+        return fail(QSA_ERR_UNSUPPORTED, "pool of %lld token rows exceeds 2^31",
+                    (long long)kv->num_pages * kv->num_kv_heads * kv->page_size);
+    out->k = static_cast<const uint16_t*>(kv->k);
+    out->v = static_cast<const uint16_t*>(kv->v);
+    out->ckey = kv->ckey;
+    out->block_table = kv->block_table;
+    out->seq_lens = kv->seq_lens;
+    out->batch = kv->batch;
+    out->Hkv = kv->num_kv_heads;
+    out->lg_ps = lg;
+    out->num_pages = kv->num_pages;
+    out->max_pages = kv->max_pages_per_seq;
+    out->max_seq_len = kv->max_seq_len;
+    return QSA_OK;
+}
+
+int check_heads(int Hq, int Hkv) {
+    if (Hq < 1) return fail(QSA_ERR_INVALID_ARG, "Hq %d < 1", Hq);
+    if (Hq % Hkv) return fail(QSA_ERR_UNSUPPORTED, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+    if (Hq / Hkv > QSA_MAX_GROUP)
+        return fail(QSA_ERR_UNSUPPORTED, "group of %d query heads per KV head exceeds %d", Hq / Hkv, QSA_MAX_GROUP);
+    return QSA_OK;
+}
+
+int check_q(const void* q, int64_t q_row_stride, int Hq) {
+    if (!q) return fail(QSA_ERR_INVALID_ARG, "q is NULL");
+    if (!aligned(q, 16)) return fail(QSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if (q_row_stride < (int64_t)Hq * QSA_HEAD_DIM || q_row_stride % 8)
+        return fail(QSA_ERR_INVALID_ARG, "q_row_stride %lld must be >= Hq * 256 and a multiple of 8",
+                    (long long)q_row_stride);
+    return QSA_OK;
+}
+
+int auto_splits(int64_t units, int k) {
+    // aim at ~1024 workgroups (4 per CU) while keeping >= 32 token slots per wave
+    int64_t s = (1024 + units - 1) / (units > 0 ? units : 1);
+    const int64_t cap = k / 32 > 1 ? k / 32 : 1;
+    if (s > cap) s = cap;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : (int)s;
+}
+
+constexpr int kAutoSplitMax = 16;
+
+}  // namespace
+
+extern "C" {
+
+int qsa_version(void) { return 100; }
+
+const char* qsa_last_error(void) { return g_err; }
+
+int qsa_compress_keys(const qsa_kv_t* kv, const int32_t* first_token, int32_t max_new_tokens, void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, true, false, true, &p)) return rc;
+    const int span = (first_token && max_new_tokens > 0 && max_new_tokens < p.max_seq_len) ? max_new_tokens
+                                                                                          : p.max_seq_len;
+    return hip_status(qsa::launch_compress(p, first_token, span, static_cast<hipStream_t>(stream)),
+                      "qsa_compress_keys");
+}
+
+int qsa_block_scores(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
+                     const int32_t* q_pos, int32_t R, int32_t Hq, float* scores, int32_t score_stride,
+                     void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, false, false, true, &p)) return rc;
+    if (int rc = check_heads(Hq, p.Hkv)) return rc;
+    if (int rc = check_q(q, q_row_stride, Hq)) return rc;
+    if (R < 0) return fail(QSA_ERR_INVALID_ARG, "R %d < 0", R);
+    if (R > 65535) return fail(QSA_ERR_UNSUPPORTED, "R %d exceeds 65535 rows per call", R);
+    if (!scores) return fail(QSA_ERR_INVALID_ARG, "scores is NULL");
+    if (score_stride < 1 || score_stride > QSA_MAX_SEQ_LEN / QSA_MICROBLOCK)
+        return fail(QSA_ERR_INVALID_ARG, "score_stride %d out of [1, %d]", score_stride,
+                    QSA_MAX_SEQ_LEN / QSA_MICROBLOCK);
+    if ((q_seq == nullptr) != (q_pos == nullptr))
+        return fail(QSA_ERR_INVALID_ARG, "q_seq and q_pos must both be given or both be NULL");
+    if (!q_seq && R != p.batch) return fail(QSA_ERR_INVALID_ARG, "decode scoring needs R == batch (%d != %d)", R, p.batch);
+    qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, q_seq, q_pos, R, Hq};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // more rows than sequences: rows share block keys, score them as a matrix product
+    const bool tiled = q_seq && R > p.batch;
+    hipError_t e = tiled ? qsa::launch_scores_tiled(p, rows, scores, score_stride, st)
+                         : qsa::launch_scores_stream(p, rows, scores, score_stride, st);
+    return hip_status(e, "qsa_block_scores");
+}
+
+int qsa_topk_blocks(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R, int32_t Hkv,
+                    int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
+    if (!scores) return fail(QSA_ERR_INVALID_ARG, "scores is NULL");
+    if (score_stride < 1 || score_stride > QSA_MAX_SEQ_LEN / QSA_MICROBLOCK)
+        return fail(QSA_ERR_INVALID_ARG, "score_stride %d out of [1, %d]", score_stride,
+                    QSA_MAX_SEQ_LEN / QSA_MICROBLOCK);
+    if (R < 0 || Hkv < 1) return fail(QSA_ERR_INVALID_ARG, "R %d / Hkv %d out of range", R, Hkv);
+    if ((int64_t)R * Hkv > 0x7fffffff) return fail(QSA_ERR_UNSUPPORTED, "R * Hkv exceeds 2^31 - 1");
+    if (k < 0 || k > QSA_MAX_TOPK) return fail(QSA_ERR_INVALID_ARG, "k %d out of [0, %d]", k, QSA_MAX_TOPK);
+    if (!sel_cnt || (k > 0 && !sel_idx)) return fail(QSA_ERR_INVALID_ARG, "sel_idx / sel_cnt is NULL");
+    return hip_status(qsa::launch_topk(scores, score_stride, q_pos, R, Hkv, k, sel_idx, sel_cnt,
+                                       static_cast<hipStream_t>(stream)),
+                      "qsa_topk_blocks");
+}
+
+size_t qsa_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t num_splits) {
+    const int64_t S = num_splits == 0 ? kAutoSplitMax : num_splits;
+    if (S <= 1 || batch <= 0 || Hq <= 0) return 0;
+    const int64_t n = S * batch * Hq;
+    const size_t out_bytes = (size_t)n * QSA_HEAD_DIM * sizeof(float);
+    const size_t lse_bytes = (size_t)n * sizeof(float);
+    return ((out_bytes + 255) & ~(size_t)255) + ((lse_bytes + 255) & ~(size_t)255);
+}
+
+int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq,
+                           const int32_t* sel_idx, const int32_t* sel_cnt, int32_t k, float scale,
+                           int32_t num_splits, void* out, int64_t out_row_stride, float* lse, float* part_out,
+                           float* part_lse, void* workspace, size_t workspace_bytes, void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, true, true, false, &p)) return rc;
+    if (int rc = check_heads(Hq, p.Hkv)) return rc;
+    if (int rc = check_q(q, q_row_stride, Hq)) return rc;
+    if (k < 0 || k > QSA_MAX_TOPK) return fail(QSA_ERR_INVALID_ARG, "k %d out of [0, %d]", k, QSA_MAX_TOPK);
+    if (!sel_cnt || (k > 0 && !sel_idx)) return fail(QSA_ERR_INVALID_ARG, "sel_idx / sel_cnt is NULL");
+    if (num_splits < 0 || num_splits > QSA_MAX_SPLITS)
+        return fail(QSA_ERR_INVALID_ARG, "num_splits %d out of [0, %d]", num_splits, QSA_MAX_SPLITS);
+    const float sc = scale > 0.f ? scale : 0.0625f;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, nullptr, nullptr, p.batch, Hq};
+    if ((int64_t)p.batch * p.Hkv * (num_splits > 0 ? num_splits : kAutoSplitMax) > 0x7fffffff)
+        return fail(QSA_ERR_UNSUPPORTED, "too many work units");
+    if (part_out) {
+        if (num_splits < 1) return fail(QSA_ERR_INVALID_ARG, "partials need num_splits >= 1");
+        if (!part_lse) return fail(QSA_ERR_INVALID_ARG, "part_lse is NULL");
+        if (!aligned(part_out, 16)) return fail(QSA_ERR_INVALID_ARG, "part_out must be 16-byte aligned");
+        qsa::AttnOut o{nullptr, 0, nullptr, part_out, part_lse};
+        return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, num_splits, o, st),
+                          "qsa_sparse_attn_decode");
+    }
+    if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
+    if (out_row_stride < (int64_t)Hq * QSA_HEAD_DIM)
+        return fail(QSA_ERR_INVALID_ARG, "out_row_stride %lld < Hq * 256", (long long)out_row_stride);
+    const int S = num_splits == 0 ? auto_splits((int64_t)p.batch * p.Hkv, k) : num_splits;
+    if (S == 1) {
+        qsa::AttnOut o{static_cast<uint16_t*>(out), out_row_stride, lse, nullptr, nullptr};
+        return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, o, st), "qsa_sparse_attn_decode");
+    }
+    if (out_row_stride != (int64_t)Hq * QSA_HEAD_DIM || !aligned(out, 8))
+        return fail(QSA_ERR_UNSUPPORTED, "a split decode writes a dense, 8-byte aligned out");
+    const size_t need = qsa_decode_workspace_bytes(p.batch, Hq, S);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(QSA_ERR_INVALID_ARG, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    const int64_t n = (int64_t)S * p.batch * Hq;
+    float* wo = static_cast<float*>(workspace);
+    float* wl = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         (((size_t)n * QSA_HEAD_DIM * sizeof(float) + 255) & ~(size_t)255));
+    qsa::AttnOut o{nullptr, 0, nullptr, wo, wl};
+    if (int rc = hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, S, o, st), "qsa_sparse_attn_decode"))
+        return rc;
+    return hip_status(qsa::launch_merge(wo, wl, S, p.batch * Hq, QSA_HEAD_DIM, static_cast<uint16_t*>(out), lse, st),
+                      "qsa_sparse_attn_decode (merge)");
+}
+
+int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
+                           const int32_t* q_pos, int32_t R, int32_t Hq, const int32_t* sel_idx,
+                           const int32_t* sel_cnt, int32_t k, float scale, void* out, int64_t out_row_stride,
+                           float* lse, void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, true, true, false, &p)) return rc;
+    if (int rc = check_heads(Hq, p.Hkv)) return rc;
+    if (int rc = check_q(q, q_row_stride, Hq)) return rc;
+    if (!q_seq || !q_pos) return fail(QSA_ERR_INVALID_ARG, "q_seq / q_pos is NULL");
+    if (R < 0) return fail(QSA_ERR_INVALID_ARG, "R %d < 0", R);
+    if ((int64_t)R * p.Hkv > 0x7fffffff) return fail(QSA_ERR_UNSUPPORTED, "R * Hkv exceeds 2^31 - 1");
+    if (k < 0 || k > QSA_MAX_TOPK) return fail(QSA_ERR_INVALID_ARG, "k %d out of [0, %d]", k, QSA_MAX_TOPK);
+    if (!sel_cnt || (k > 0 && !sel_idx)) return fail(QSA_ERR_INVALID_ARG, "sel_idx / sel_cnt is NULL");
+    if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
+    if (out_row_stride < (int64_t)Hq * QSA_HEAD_DIM)
+        return fail(QSA_ERR_INVALID_ARG, "out_row_stride %lld < Hq * 256", (long long)out_row_stride);
+    const float sc = scale > 0.f ? scale : 0.0625f;
+    qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, q_seq, q_pos, R, Hq};
+    qsa::AttnOut o{static_cast<uint16_t*>(out), out_row_stride, lse, nullptr, nullptr};
+    return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, o, static_cast<hipStream_t>(stream)),
+                      "qsa_sparse_attn_extend");
+}
+
+int qsa_merge_lse(const float* part_out, const float* part_lse, int32_t S, int32_t N, int32_t D, void* out_bf16,
+                  float* out_lse, void* stream) {
+    if (!part_out || !part_lse || !out_bf16) return fail(QSA_ERR_INVALID_ARG, "part_out / part_lse / out is NULL");
+    if (S < 1 || S > QSA_MAX_SPLITS) return fail(QSA_ERR_INVALID_ARG, "S %d out of [1, %d]", S, QSA_MAX_SPLITS);
+    if (N < 0) return fail(QSA_ERR_INVALID_ARG, "N %d < 0", N);
+    if (D < 4 || D > 1024 || D % 4) return fail(QSA_ERR_UNSUPPORTED, "D %d must be a multiple of 4 in [4, 1024]", D);
+    if (!aligned(part_out, 16) || !aligned(out_bf16, 8))
+        return fail(QSA_ERR_INVALID_ARG, "part_out must be 16-byte and out 8-byte aligned");
+    return hip_status(qsa::launch_merge(part_out, part_lse, S, N, D, static_cast<uint16_t*>(out_bf16), out_lse,
+                                        static_cast<hipStream_t>(stream)),
+                      "qsa_merge_lse");
+}
+
+}  // extern "C"

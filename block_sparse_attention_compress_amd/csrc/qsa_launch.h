@@ -1,0 +1,53 @@
+// Host-side launchers of the QSA kernels.  Arguments are validated by the
+// C ABI layer (qsa_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct PagedKV {
+    const uint16_t* k;
+    const uint16_t* v;
+    float* ckey;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int batch, Hkv, lg_ps, num_pages, max_pages, max_seq_len;
+};
+
+struct Rows {
+    const uint16_t* q;        // bf16 [R] rows of [Hq][256]
+    int64_t q_stride;         // elements between rows
+    const int32_t* q_seq;     // NULL: row r is sequence r
+    const int32_t* q_pos;     // NULL: t = L - 1
+    int R, Hq;
+};
+
+// span: host bound on the tokens per sequence from first_token on
+hipError_t launch_compress(const PagedKV& kv, const int32_t* first_token, int span, hipStream_t st);
+
+hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
+                                hipStream_t st);
+hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
+                               hipStream_t st);
+
+hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,
+                       int32_t* sel_idx, int32_t* sel_cnt, hipStream_t st);
+
+struct AttnOut {
+    uint16_t* out;            // bf16, final result (num_splits == 1 and part_out == NULL)
+    int64_t out_stride;
+    float* lse;               // [R][Hq] or NULL
+    float* part_out;          // fp32 [S][R][Hq][256] (partials)
+    float* part_lse;          // fp32 [S][R][Hq]
+};
+
+hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt, int k,
+                       float scale, int num_splits, const AttnOut& o, hipStream_t st);
+
+hipError_t launch_merge(const float* part_out, const float* part_lse, int S, int N, int D, uint16_t* out,
+                        float* out_lse, hipStream_t st);
+
+}  // namespace qsa

@@ -1,0 +1,216 @@
+// a2 -- block scores: s[r][h][b] = (sum of the group's query heads) . ckey[b].
+//
+// The indexer scores the compressed blocks against the query ("Qwen 4 QSA
+// krijgt decode-contextparallellisme", section "Wat de pull request
+// daadwerkelijk verandert"); the pages do not say how the query heads of a KV
+// group are combined, and the library scores with their sum (one selection per
+// KV head).  Scores are left unscaled: the softmax scale does not change the
+// order.
+//
+// Two kernels, both fp32:
+//  * scores_stream_kernel (decode): one row reads its whole block-key list once.
+//    This is the dominant HBM stream of a decode step.  A wave takes 16 blocks
+//    (16 KiB) at a time, each lane one float4 of each block, and folds the 16
+//    dot products with a reduce-scatter butterfly (17 lane exchanges for 16
+//    blocks instead of 16 x 6).
+//  * scores_tiled_kernel (extend): many query rows share one sequence, so the
+//    scores are a dense [rows x 256] . [256 x blocks] product; 16x16x4 fp32
+//    matrix-core tiles, 16 rows per wave.
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace qsa {
+
+constexpr int kStreamChunk = 256;  // blocks per workgroup (4 waves x 64)
+
+__global__ __launch_bounds__(256) void scores_stream_kernel(
+    const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int g, const float* __restrict__ ckey, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages, float* __restrict__ scores,
+    int score_stride) {
+    const int row = blockIdx.z;
+    const int h = blockIdx.y;
+    const int seq = q_seq ? q_seq[row] : row;
+    const int L = seq_lens[seq];
+    const int t = q_pos ? q_pos[row] : L - 1;
+    if (t < 0) return;
+    const int n_elig = min(t / 4 + 1, score_stride);
+    const int chunk0 = blockIdx.x * kStreamChunk;
+    if (chunk0 >= n_elig) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+
+    // group-summed query: lane holds dims 4*lane .. 4*lane+3
+    float4 qs = make_float4(0.f, 0.f, 0.f, 0.f);
+    const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + 4 * lane;
+    for (int j = 0; j < g; ++j) {
+        const uint2 w = *reinterpret_cast<const uint2*>(qrow + j * kHeadDim);
+        qs.x += bf16_lo(w.x);
+        qs.y += bf16_hi(w.x);
+        qs.z += bf16_lo(w.y);
+        qs.w += bf16_hi(w.y);
+    }
+
+    const int lg_bpp = lg_ps - 2;  // blocks per page = page_size / 4
+    float* srow = scores + ((int64_t)row * Hkv + h) * score_stride;
+    for (int grp = 0; grp < 4; ++grp) {
+        const int b0 = chunk0 + wave * 64 + grp * 16;
+        if (b0 >= n_elig) break;
+        float4 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int b = b0 + j;
+            if (b < n_elig) {
+                const int64_t page = block_table[(int64_t)seq * max_pages + (b >> lg_bpp)];
+                const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
+                v[j] = *reinterpret_cast<const float4*>(ckey + brow * kHeadDim + 4 * lane);
+            } else {
+                v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        float p[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = qs.x * v[j].x + qs.y * v[j].y + qs.z * v[j].z + qs.w * v[j].w;
+        // reduce-scatter: after the step across lane bit m (m = 5, 4, 3, 2) a lane
+        // keeps the half of its blocks selected by that bit; finally lane l holds
+        // the full sum of block l >> 2 (lanes differing in bits 0, 1 agree).
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool up = lane & 32;
+            const float keep = up ? p[i + 8] : p[i], send = up ? p[i] : p[i + 8];
+            p[i] = keep + __shfl_xor(send, 32);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool up = lane & 16;
+            const float keep = up ? p[i + 4] : p[i], send = up ? p[i] : p[i + 4];
+            p[i] = keep + __shfl_xor(send, 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bool up = lane & 8;
+            const float keep = up ? p[i + 2] : p[i], send = up ? p[i] : p[i + 2];
+            p[i] = keep + __shfl_xor(send, 8);
+        }
+        {
+            const bool up = lane & 4;
+            const float keep = up ? p[1] : p[0], send = up ? p[0] : p[1];
+            p[0] = keep + __shfl_xor(send, 4);
+        }
+        p[0] += __shfl_xor(p[0], 2);
+        p[0] += __shfl_xor(p[0], 1);
+        const int b = b0 + (lane >> 2);
+        if ((lane & 3) == 0 && b < n_elig) srow[b] = p[0];
+    }
+}
+
+// Extend: 64 rows per workgroup, 16 per wave.  Lane (c = lane & 15, kq = lane >> 4)
+// holds, at k-step m, qsum[row c][64 kq + m] (A operand) and
+// ckey[block c][64 kq + m] (B operand): the same dim for A and B, so the 64
+// steps of the 16x16x4 matrix-core op cover all 256 dims.  Output element i of
+// the lane is row 4 kq + i, block c of the tile.  Rows of one wave that belong to
+// different sequences are scored in separate passes.
+__global__ __launch_bounds__(256) void scores_tiled_kernel(
+    const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int R, int g, const float* __restrict__ ckey,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages,
+    float* __restrict__ scores, int score_stride) {
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int r0 = blockIdx.x * 64 + wave * 16;
+    if (r0 >= R) return;
+    const int c = lane & 15, kq = lane >> 4;
+    const int row = r0 + c;
+    const bool valid = row < R;
+    const int seq_r = valid ? q_seq[row] : -1;
+    const int t_r = valid ? q_pos[row] : -1;
+
+    float a[64];
+#pragma unroll
+    for (int m = 0; m < 64; ++m) a[m] = 0.f;
+    if (valid) {
+        const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + 64 * kq;
+        for (int j = 0; j < g; ++j) {
+            const uint4* p = reinterpret_cast<const uint4*>(qrow + j * kHeadDim);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 w = p[i];
+                a[8 * i + 0] += bf16_lo(w.x);
+                a[8 * i + 1] += bf16_hi(w.x);
+                a[8 * i + 2] += bf16_lo(w.y);
+                a[8 * i + 3] += bf16_hi(w.y);
+                a[8 * i + 4] += bf16_lo(w.z);
+                a[8 * i + 5] += bf16_hi(w.z);
+                a[8 * i + 6] += bf16_lo(w.w);
+                a[8 * i + 7] += bf16_hi(w.w);
+            }
+        }
+    }
+    const int lg_bpp = lg_ps - 2;
+    const uint64_t row_lanes = __ballot(valid && kq == 0 && t_r >= 0) & 0xffffull;
+    uint64_t pending = row_lanes;
+    while (pending) {
+        const int first = __builtin_ctzll(pending);
+        const int s = __shfl(seq_r, first);
+        const uint64_t active = __ballot(kq == 0 && valid && t_r >= 0 && seq_r == s) & 0xffffull;
+        pending &= ~active;
+        const int L = seq_lens[s];
+        const int nb_seq = (L + 3) >> 2;
+        const int ne_c = ((active >> c) & 1) ? min(t_r / 4 + 1, score_stride) : 0;
+        const int n_max = wave_max_int(ne_c);
+        int ne_out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ne_out[i] = __shfl(ne_c, 4 * kq + i);
+        for (int bt0 = 0; bt0 < n_max; bt0 += 16) {
+            const int b = bt0 + c;
+            float bv[64];
+            if (b < nb_seq) {
+                const int64_t page = block_table[(int64_t)s * max_pages + (b >> lg_bpp)];
+                const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
+                const float4* src = reinterpret_cast<const float4*>(ckey + brow * kHeadDim + 64 * kq);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float4 w = src[i];
+                    bv[4 * i] = w.x;
+                    bv[4 * i + 1] = w.y;
+                    bv[4 * i + 2] = w.z;
+                    bv[4 * i + 3] = w.w;
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < 64; ++m) bv[m] = 0.f;
+            }
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 64; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], bv[m], acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 4 * kq + i;
+                if (b < ne_out[i]) scores[((int64_t)(r0 + rr) * Hkv + h) * score_stride + b] = acc[i];
+            }
+        }
+    }
+}
+
+hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
+                                hipStream_t st) {
+    if (rows.R == 0) return hipSuccess;
+    dim3 grid((score_stride + kStreamChunk - 1) / kStreamChunk, kv.Hkv, rows.R);
+    hipLaunchKernelGGL(scores_stream_kernel, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq, rows.q_pos,
+                       rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps, kv.max_pages, scores,
+                       score_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
+                               hipStream_t st) {
+    if (rows.R == 0) return hipSuccess;
+    dim3 grid((rows.R + 63) / 64, kv.Hkv);
+    hipLaunchKernelGGL(scores_tiled_kernel, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq, rows.q_pos,
+                       rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,
+                       kv.max_pages, scores, score_stride);
+    return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,95 @@
+"""Step drivers: the QSA decode and extend passes as sequences of libqsa calls.
+
+Buffers are torch tensors on the current device (plumbing); every step runs in
+the library's HIP kernels, in the order of the method -- block keys, block
+scores, top-k selection, sparse attention, log-sum-exp merge.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import (HEAD_DIM, KVCache, qsa_block_scores, qsa_compress_keys, qsa_decode_workspace_bytes,
+               qsa_sparse_attn_decode, qsa_sparse_attn_extend, qsa_topk_blocks)
+
+
+@dataclass
+class DecodeBuffers:
+    """Intermediate and output buffers of one decode step."""
+
+    scores: torch.Tensor      # fp32 [B][Hkv][score_stride]
+    sel_idx: torch.Tensor     # int32 [B][Hkv][k]
+    sel_cnt: torch.Tensor     # int32 [B][Hkv]
+    out: torch.Tensor         # bf16 [B][Hq][256]
+    lse: torch.Tensor         # fp32 [B][Hq]
+    workspace: Optional[torch.Tensor]
+    score_stride: int
+    k: int
+
+    @staticmethod
+    def allocate(B: int, Hq: int, Hkv: int, score_stride: int, k: int, num_splits: int = 0,
+                 device="cuda") -> "DecodeBuffers":
+        ws_bytes = qsa_decode_workspace_bytes(B, Hq, num_splits)
+        return DecodeBuffers(
+            scores=torch.empty((B, Hkv, score_stride), dtype=torch.float32, device=device),
+            sel_idx=torch.empty((B, Hkv, max(k, 1)), dtype=torch.int32, device=device),
+            sel_cnt=torch.empty((B, Hkv), dtype=torch.int32, device=device),
+            out=torch.empty((B, Hq, HEAD_DIM), dtype=torch.bfloat16, device=device),
+            lse=torch.empty((B, Hq), dtype=torch.float32, device=device),
+            workspace=torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None,
+            score_stride=score_stride, k=k)
+
+
+def decode_step(kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: DecodeBuffers, scale: float = 0.0,
+                num_splits: int = 0, refresh_keys: bool = True, stream=None) -> None:
+    """One decode step for every sequence of `kv`: refresh the block key holding the
+    newest token (q_pos = L - 1), score, select, attend (and merge the splits).
+    q: bf16 [B][Hq][256] (rows may be strided)."""
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv = kv.k.shape[1]
+    if refresh_keys:
+        qsa_compress_keys(kv, q_pos, 1, stream=stream)
+    qsa_block_scores(kv, q, q.stride(0), None, None, B, Hq, buf.scores, buf.score_stride, stream=stream)
+    qsa_topk_blocks(buf.scores, buf.score_stride, q_pos, B, Hkv, buf.k, buf.sel_idx, buf.sel_cnt, stream=stream)
+    ws = buf.workspace
+    qsa_sparse_attn_decode(kv, q, q.stride(0), Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale, num_splits, buf.out,
+                           buf.out.stride(0), buf.lse, workspace=ws, workspace_bytes=0 if ws is None else ws.numel(),
+                           stream=stream)
+
+
+@dataclass
+class ExtendBuffers:
+    scores: torch.Tensor      # fp32 [R][Hkv][score_stride]
+    sel_idx: torch.Tensor     # int32 [R][Hkv][k]
+    sel_cnt: torch.Tensor     # int32 [R][Hkv]
+    out: torch.Tensor         # bf16 [R][Hq][256]
+    lse: torch.Tensor         # fp32 [R][Hq]
+    score_stride: int
+    k: int
+
+    @staticmethod
+    def allocate(R: int, Hq: int, Hkv: int, score_stride: int, k: int, device="cuda") -> "ExtendBuffers":
+        return ExtendBuffers(
+            scores=torch.empty((R, Hkv, score_stride), dtype=torch.float32, device=device),
+            sel_idx=torch.empty((R, Hkv, max(k, 1)), dtype=torch.int32, device=device),
+            sel_cnt=torch.empty((R, Hkv), dtype=torch.int32, device=device),
+            out=torch.empty((R, Hq, HEAD_DIM), dtype=torch.bfloat16, device=device),
+            lse=torch.empty((R, Hq), dtype=torch.float32, device=device),
+            score_stride=score_stride, k=k)
+
+
+def extend_step(kv: KVCache, q: torch.Tensor, q_seq: torch.Tensor, q_pos: torch.Tensor, buf: ExtendBuffers,
+                first_new: Optional[torch.Tensor] = None, max_new_tokens: int = 0, scale: float = 0.0,
+                stream=None) -> None:
+    """One extend chunk: block keys of the new tokens (first_new [B] = first new
+    position per sequence), then per-row scores, selection and attention."""
+    R, Hq = q.shape[0], q.shape[1]
+    Hkv = kv.k.shape[1]
+    if first_new is not None:
+        qsa_compress_keys(kv, first_new, max_new_tokens, stream=stream)
+    qsa_block_scores(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.scores, buf.score_stride, stream=stream)
+    qsa_topk_blocks(buf.scores, buf.score_stride, q_pos, R, Hkv, buf.k, buf.sel_idx, buf.sel_cnt, stream=stream)
+    qsa_sparse_attn_extend(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale, buf.out,
+                           buf.out.stride(0), buf.lse, stream=stream)

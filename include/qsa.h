@@ -1,0 +1,199 @@
+/*
+ * qsa.h -- C ABI of libqsa.so, the MI355X (gfx950) hot path of QSA
+ * micro-block sparse attention.
+ *
+ * The method: a light indexer compresses the keys of a sequence into
+ * microblocks of 4 tokens, scores every block against the query, keeps the
+ * best 512 blocks (about 2048 token positions), and exact softmax attention
+ * then runs over the uncompressed K and V of only those tokens ("Qwen 4 QSA
+ * krijgt decode-contextparallellisme", section "Wat de pull request
+ * daadwerkelijk verandert").  The same page splits the main KV read into
+ * partitions whose partial attention results are combined at the end; here
+ * the partitions are split-KV work units on one GPU merged by log-sum-exp.
+ * Head dimension 256 in bf16 and the (query, KV) head pairs (16,2), (24,2),
+ * (12,1), (6,1), (3,1) come from "Qwen4-Exp QSA komt naar Huawei's Ascend",
+ * section "Wat de pull request daadwerkelijk toevoegt".
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *    the qsa_kv_t descriptor itself, which lives in host memory.  The library
+ *    never allocates device memory and keeps no pointer after a call returns.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  No call synchronises or copies device -> host, so every call
+ *    may be captured in a HIP graph.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    rejected call launches nothing and returns QSA_ERR_INVALID_ARG or
+ *    QSA_ERR_UNSUPPORTED.  There is no silent fallback.  Contents of device
+ *    buffers (block tables, lengths, selections) are trusted: they must obey
+ *    the rules stated below.
+ *  - qsa_last_error() describes the most recent failure on the calling thread.
+ *
+ * Notation: B sequences, Hq query heads, Hkv KV heads, g = Hq / Hkv (query
+ * head j belongs to KV head j / g), D = 256, L_i the length of sequence i,
+ * nb_i = ceil(L_i / 4) blocks.  A query row r has a sequence q_seq[r] and a
+ * position t = q_pos[r] (decode: one row per sequence with t = L_i - 1).
+ * Block b is eligible for the row iff 4b <= t.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_API __attribute__((visibility("default")))
+
+#define QSA_OK 0
+#define QSA_ERR_INVALID_ARG (-1) /* bad pointer, size, stride or range */
+#define QSA_ERR_UNSUPPORTED (-2) /* valid but outside what the kernels handle */
+#define QSA_ERR_HIP (-3)         /* a HIP launch reported an error */
+
+#define QSA_HEAD_DIM 256
+#define QSA_MICROBLOCK 4
+#define QSA_DEFAULT_TOPK 512
+#define QSA_MAX_TOPK 2048
+#define QSA_MAX_GROUP 16            /* query heads per KV head */
+#define QSA_MAX_SPLITS 64
+#define QSA_MAX_SEQ_LEN (1 << 20)   /* tokens per sequence */
+
+/*
+ * Paged KV cache.  Page p of the pool holds, for every KV head, page_size
+ * consecutive tokens of one sequence:
+ *   k, v   bf16  [num_pages][Hkv][page_size][256]
+ *   ckey   fp32  [num_pages][Hkv][page_size / 4][256]   block keys, paged by
+ *                the same block table, so a page's keys and block keys never
+ *                diverge (the DCP page keeps selector and main cache in one
+ *                cache group for that reason).
+ *   block_table int32 [batch][max_pages_per_seq]: token i of sequence s lives
+ *                in page block_table[s][i / page_size], slot i % page_size.
+ *   seq_lens    int32 [batch]: L_s, 0 <= L_s <= max_seq_len.
+ * page_size is a power of two >= 4 (a contiguous cache is one page of
+ * page_size >= max_seq_len with an identity table).  max_seq_len is a host
+ * bound on every L_s, used to size grids.
+ */
+typedef struct qsa_kv {
+    const void* k;
+    const void* v;
+    float* ckey;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int32_t batch;
+    int32_t num_kv_heads;
+    int32_t head_dim;        /* must be 256 */
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t max_pages_per_seq;
+    int32_t max_seq_len;
+} qsa_kv_t;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+QSA_API int qsa_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+QSA_API const char* qsa_last_error(void);
+
+/*
+ * a1 -- block keys.  For every sequence s and KV head h, and every block b
+ * with 4b < L_s and 4b + 3 >= first_token[s] (first_token NULL = 0), writes
+ *   ckey[b] = fp32 mean of the block's n = min(4, L_s - 4b) keys,
+ * computed exactly as ((k0 + k1) + (k2 + k3)) * 0.25 for n = 4 and as the
+ * left-to-right sum divided by n (correctly rounded) for n < 4.  The pages
+ * say only that keys are compressed into 4-token microblocks; this pooling is
+ * the stated reading.  Idempotent: a page shared by two sequences gets the
+ * same values from both.  Decode calls it with first_token = L_s - 1 to
+ * refresh the block holding the newest token; extend with the first new
+ * position.  max_new_tokens is a host bound on L_s - first_token[s] used to
+ * size the grid (<= 0: max_seq_len); it is ignored when first_token is NULL.
+ */
+QSA_API int qsa_compress_keys(const qsa_kv_t* kv, const int32_t* first_token, int32_t max_new_tokens,
+                              void* stream);
+
+/*
+ * a2 -- block scores.  q: bf16 rows, row r at q + r * q_row_stride
+ * (elements), heads contiguous inside a row ([Hq][256]).  q_seq / q_pos
+ * (int32 [R]) give each row's sequence and position; both may be NULL for
+ * decode (row r = sequence r at t = L_r - 1, R must equal batch).  Writes
+ *   scores[(r * Hkv + h) * score_stride + b] = (sum_{j in group h} q[r][j]) . ckey[b]
+ * in fp32 for b < n_elig(r) = min(t / 4 + 1, score_stride); entries at or
+ * after n_elig(r) are not written.  The scale is not applied (it does not
+ * change the order).  Rows sharing a sequence are scored with matrix cores
+ * when there are more rows than sequences (extend).  R <= 65535 per call.
+ */
+QSA_API int qsa_block_scores(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
+                     const int32_t* q_pos, int32_t R, int32_t Hq, float* scores, int32_t score_stride,
+                     void* stream);
+
+/*
+ * a3 -- top-k selection.  For each (row, KV head): among the n_elig(r)
+ * scores (q_pos as above; NULL means n_elig = score_stride for every row),
+ * keeps the k largest under the order (score descending, block index
+ * ascending; -0 equals +0), and writes them in ascending block order to
+ *   sel_idx[(r * Hkv + h) * k + j], j < cnt, then -1 up to k,
+ *   sel_cnt[r * Hkv + h] = cnt = min(k, n_elig(r)).
+ * 0 <= k <= QSA_MAX_TOPK.  Scores must be finite.
+ */
+QSA_API int qsa_topk_blocks(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R, int32_t Hkv,
+                    int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* stream);
+
+/*
+ * a4 -- sparse attention, decode (one row per sequence at t = L_s - 1).
+ * sel_idx / sel_cnt as written by qsa_topk_blocks ([batch][Hkv][k], ascending,
+ * every block eligible).  For query head j of KV head h the token set is
+ *   T = { 4b + u : b selected, 0 <= u < 4, 4b + u < L_s }
+ * and the result is softmax(scale * q_j . K_T^T) . V_T with an fp32 online
+ * softmax; scale <= 0 selects 1/sqrt(256) = 1/16.  An empty T gives output 0
+ * and lse = -inf (fully masked rows keep a zero output, as on the Ascend page).
+ *
+ * Split-KV: the selected tokens, in order, have ranks p = 0..|T|-1; split s
+ * of S takes the tokens with p mod S == s.
+ *  - part_out != NULL: num_splits = S >= 1 partials are written,
+ *      part_out fp32 [S][batch][Hq][256] (normalised), part_lse fp32 [S][batch][Hq]
+ *    (natural log); out / lse are not touched.  qsa_merge_lse combines them.
+ *  - part_out == NULL: the final result is written, out bf16 at
+ *    out + row * out_row_stride ([Hq][256] per row), lse fp32 [batch][Hq]
+ *    (lse may be NULL).  num_splits = 0 lets the library choose the split
+ *    count; any S > 1 is merged internally through `workspace`, which must
+ *    hold qsa_decode_workspace_bytes(batch, Hq, num_splits) bytes.
+ */
+QSA_API int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq,
+                           const int32_t* sel_idx, const int32_t* sel_cnt, int32_t k, float scale,
+                           int32_t num_splits, void* out, int64_t out_row_stride, float* lse, float* part_out,
+                           float* part_lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes qsa_sparse_attn_decode needs for num_splits (0 = the
+ * library's own choice) when it writes the final result. */
+QSA_API size_t qsa_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t num_splits);
+
+/*
+ * a6 -- sparse attention, extend.  Like decode, but every query row r has its
+ * own sequence q_seq[r], position t = q_pos[r] and selection, and tokens
+ * after t are masked: T = { 4b + u : b selected, 4b + u < L, 4b + u <= t }.
+ * Writes out (bf16, row stride out_row_stride) and lse ([R][Hq], may be NULL).
+ * The g heads of a KV head are padded to 16 matrix-core rows in the kernel;
+ * the padded rows are discarded (the Ascend page pads 12 -> 16 for its tiler).
+ */
+QSA_API int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
+                           const int32_t* q_pos, int32_t R, int32_t Hq, const int32_t* sel_idx,
+                           const int32_t* sel_cnt, int32_t k, float scale, void* out, int64_t out_row_stride,
+                           float* lse, void* stream);
+
+/*
+ * a5 -- log-sum-exp merge of S partial results (the combine step of decode
+ * context parallelism on the DCP page, section on how it differs from tensor
+ * parallelism):  part_out fp32 [S][N][D], part_lse fp32 [S][N] ->
+ *   lse = M + ln sum_s exp(lse_s - M),  M = max_s lse_s,
+ *   out = sum_s exp(lse_s - lse) * o_s   (bf16 [N][D]),
+ * all partials -inf -> out 0, lse -inf.  1 <= S <= QSA_MAX_SPLITS,
+ * D a multiple of 4 up to 1024.  out_lse may be NULL.
+ */
+QSA_API int qsa_merge_lse(const float* part_out, const float* part_lse, int32_t S, int32_t N, int32_t D, void* out_bf16,
+                  float* out_lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

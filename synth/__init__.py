@@ -251,6 +251,31 @@ class Case:
         return np.ascontiguousarray(pool[pages, :, slots, :].transpose(1, 0, 2))
 
 
+def to_device(case: Case, device="cuda", ckey: bool = True):
+    """Upload a case's paged pool, tables and queries as torch tensors (layout only).
+
+    Returns a dict: k, v (bf16 [num_pages][Hkv][page_size][D]), ckey (fp32, zeroed),
+    block_table, seq_lens, q_seq, q_pos (int32), q (bf16 [R][Hq][D])."""
+    import torch
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+
+    out = {
+        "k": bf16(case.paged("k")),
+        "v": bf16(case.paged("v")),
+        "block_table": torch.from_numpy(case.block_table).to(device),
+        "seq_lens": torch.from_numpy(case.lens).to(device),
+        "q_seq": torch.from_numpy(case.q_seq).to(device),
+        "q_pos": torch.from_numpy(case.q_pos).to(device),
+        "q": bf16(case.q),
+    }
+    if ckey:
+        out["ckey"] = torch.zeros((case.num_pages, case.Hkv, case.page_size // 4, case.D), dtype=torch.float32,
+                                  device=device)
+    return out
+
+
 def _block_table(seed: int, lens: np.ndarray, page_size: int, shuffle: bool, shared_prefix_pages: int):
     npg = [(int(L) + page_size - 1) // page_size for L in lens]
     max_pages = max(max(npg) if npg else 1, 1)

@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point,
+and rejects bad arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_compress_amd as qsa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qsa.h")
+
+# fake but well-aligned device addresses: validation never dereferences them and a
+# rejected call launches nothing
+P = 0x10000
+
+
+def declared():
+    text = open(HEADER).read()
+    return re.findall(r"QSA_API\s+[\w\s\*]+?\b(qsa_\w+)\s*\(", text)
+
+
+def kv(**over):
+    f = dict(k=P, v=P, ckey=P, block_table=P, seq_lens=P, batch=2, num_kv_heads=2, head_dim=256, page_size=64,
+             num_pages=100, max_pages_per_seq=50, max_seq_len=3200)
+    f.update(over)
+    return qsa.qsa_kv_t(**f)
+
+
+def status(fn, *args):
+    return getattr(qsa.lib(), fn)(*args)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared()
+    assert set(names) == set(qsa.EXPORTS)
+    lib = ctypes.CDLL(qsa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert qsa.qsa_version() >= 100
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (QSA_\w+) \(?(-?\d+)", text))
+    assert int(consts["QSA_HEAD_DIM"]) == qsa.HEAD_DIM == 256
+    assert int(consts["QSA_MICROBLOCK"]) == qsa.MICROBLOCK == 4
+    assert int(consts["QSA_DEFAULT_TOPK"]) == qsa.DEFAULT_TOPK == 512
+    assert int(consts["QSA_MAX_TOPK"]) == qsa.MAX_TOPK
+    assert int(consts["QSA_ERR_INVALID_ARG"]) == qsa.QSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=None), qsa.QSA_ERR_INVALID_ARG),
+    (dict(ckey=None), qsa.QSA_ERR_INVALID_ARG),
+    (dict(block_table=None), qsa.QSA_ERR_INVALID_ARG),
+    (dict(head_dim=128), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(page_size=48), qsa.QSA_ERR_INVALID_ARG),
+    (dict(page_size=2), qsa.QSA_ERR_INVALID_ARG),
+    (dict(max_seq_len=(1 << 20) + 1, max_pages_per_seq=20000), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(max_pages_per_seq=10), qsa.QSA_ERR_INVALID_ARG),      # 10 * 64 < 3200
+    (dict(num_pages=1 << 24), qsa.QSA_ERR_UNSUPPORTED),          # 2^24 pages x 2 heads x 64 rows = 2^31
+    (dict(k=P + 8), qsa.QSA_ERR_INVALID_ARG),                    # misaligned
+    (dict(batch=-1), qsa.QSA_ERR_INVALID_ARG),
+])
+def test_compress_rejects(over, code):
+    d = kv(**over)
+    assert status("qsa_compress_keys", ctypes.byref(d), None, 0, None) == code
+    assert qsa.qsa_last_error() != ""
+
+
+def test_scores_rejects_null_q():
+    d = kv()
+    assert status("qsa_block_scores", ctypes.byref(d), None, 4096, None, None, 2, 8, P, 800, None) == \
+        qsa.QSA_ERR_INVALID_ARG
+
+
+def test_scores_head_and_stride_checks():
+    d = kv()
+    L = "qsa_block_scores"
+    # Hq not a multiple of Hkv
+    assert status(L, ctypes.byref(d), P, 2048, None, None, 2, 7, P, 800, None) == qsa.QSA_ERR_UNSUPPORTED
+    # group of 18 > 16
+    assert status(L, ctypes.byref(d), P, 36 * 256, None, None, 2, 36, P, 800, None) == qsa.QSA_ERR_UNSUPPORTED
+    # row stride below Hq * 256, or not a multiple of 8
+    assert status(L, ctypes.byref(d), P, 1000, None, None, 2, 8, P, 800, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, ctypes.byref(d), P, 2052, None, None, 2, 8, P, 800, None) == qsa.QSA_ERR_INVALID_ARG
+    # decode mode needs R == batch
+    assert status(L, ctypes.byref(d), P, 2048, None, None, 3, 8, P, 800, None) == qsa.QSA_ERR_INVALID_ARG
+    # q_seq without q_pos
+    assert status(L, ctypes.byref(d), P, 2048, P, None, 2, 8, P, 800, None) == qsa.QSA_ERR_INVALID_ARG
+    # score_stride out of range
+    assert status(L, ctypes.byref(d), P, 2048, None, None, 2, 8, P, 0, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, ctypes.byref(d), P, 2048, None, None, 2, 8, P, (1 << 18) + 1, None) == qsa.QSA_ERR_INVALID_ARG
+
+
+def test_topk_rejects():
+    L = "qsa_topk_blocks"
+    assert status(L, None, 100, None, 2, 2, 16, P, P, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 100, None, 2, 2, 2049, P, P, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 100, None, 2, 2, -1, P, P, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 100, None, 2, 2, 16, None, P, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 100, None, 2, 2, 16, P, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 100, None, 2, 0, 16, P, P, None) == qsa.QSA_ERR_INVALID_ARG
+
+
+def test_decode_rejects():
+    d = kv()
+    f = qsa.lib().qsa_sparse_attn_decode
+    base = [ctypes.byref(d), P, 4096, 16, P, P, 512, 0.0, 0, P, 4096, P, None, None, P, 1 << 30, None]
+
+    def call(**ch):
+        a = list(base)
+        names = ["kv", "q", "qs", "Hq", "sel", "cnt", "k", "scale", "S", "out", "os", "lse", "po", "pl", "ws", "wb", "st"]
+        for n, v in ch.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    assert call(k=4096) == qsa.QSA_ERR_INVALID_ARG
+    assert call(S=65) == qsa.QSA_ERR_INVALID_ARG
+    assert call(cnt=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(out=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(os=100) == qsa.QSA_ERR_INVALID_ARG
+    assert call(po=P, S=0) == qsa.QSA_ERR_INVALID_ARG          # partials need S >= 1
+    assert call(po=P, pl=None, S=4) == qsa.QSA_ERR_INVALID_ARG
+    assert call(ws=None, S=4) == qsa.QSA_ERR_INVALID_ARG        # split merge needs a workspace
+    assert call(wb=16, S=4) == qsa.QSA_ERR_INVALID_ARG
+    assert call(os=8192, S=4) == qsa.QSA_ERR_UNSUPPORTED        # split merge writes dense rows
+    dv = kv(v=None)
+    assert f(ctypes.byref(dv), *base[1:]) == qsa.QSA_ERR_INVALID_ARG
+
+
+def test_extend_and_merge_reject():
+    d = kv()
+    f = qsa.lib().qsa_sparse_attn_extend
+    assert f(ctypes.byref(d), P, 4096, None, P, 10, 16, P, P, 512, 0.0, P, 4096, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), P, 4096, P, P, -1, 16, P, P, 512, 0.0, P, 4096, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), P, 4096, P, P, 10, 48, P, P, 512, 0.0, P, 48 * 256, None, None) == qsa.QSA_ERR_UNSUPPORTED
+    m = qsa.lib().qsa_merge_lse
+    assert m(P, P, 0, 10, 256, P, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert m(P, P, 65, 10, 256, P, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert m(P, P, 4, 10, 250, P, None, None) == qsa.QSA_ERR_UNSUPPORTED
+    assert m(P, P, 4, 10, 2048, P, None, None) == qsa.QSA_ERR_UNSUPPORTED
+    assert m(None, P, 4, 10, 256, P, None, None) == qsa.QSA_ERR_INVALID_ARG
+
+
+def test_workspace_size_formula():
+    # S partials of [B][Hq][256] fp32 plus [B][Hq] lse, each rounded up to 256 bytes
+    S, B, Hq = 4, 3, 6
+    n = S * B * Hq
+    want = ((n * 256 * 4 + 255) // 256) * 256 + ((n * 4 + 255) // 256) * 256
+    assert qsa.qsa_decode_workspace_bytes(B, Hq, S) == want
+    assert qsa.qsa_decode_workspace_bytes(B, Hq, 1) == 0
+    assert qsa.qsa_decode_workspace_bytes(B, Hq, 0) >= qsa.qsa_decode_workspace_bytes(B, Hq, 16)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(qsa, "_lib", None)
+    monkeypatch.setattr(qsa, "LIB_PATH", str(tmp_path / "libqsa.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        qsa.lib()
