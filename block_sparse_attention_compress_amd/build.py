@@ -27,6 +27,9 @@ CFLAGS = [
     "-fvisibility=hidden",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in arch VGPRs: with them in AGPRs the attention loop
+    # copied all 64 of them out and back every tile around the rare rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

@@ -10,18 +10,25 @@
 //
 // Work unit = one workgroup of 4 waves per (row, KV head, split).  The g query
 // heads of the KV head form the 16 rows of a matrix-core tile (g <= 16; extra rows
-// are zero and discarded, as the Ascend page pads 12 -> 16 heads).  A wave takes
-// 32 selected tokens at a time:
-//   S^T[token][head] = K . Q^T   8 x v_mfma_f32_16x16x32_bf16 per 16 tokens
-//                                (lane (r, q) reads 128 contiguous bytes of the
-//                                K row of token r, A operand; Q is the B operand)
-//   online softmax in fp32, base 2 (x * scale * log2 e)
-//   O[head][dim] += P . V        16 x v_mfma_f32_16x16x32_bf16 per 32 tokens
-//                                (P rounded to bf16; lane (c, q) reads 32
-//                                contiguous bytes of 8 V rows -- the tokens it
-//                                holds in P -- and dim 16c + n feeds output tile n)
-// The 4 waves' (m, l, O) are merged in LDS and written as the final bf16 output
-// or as an fp32 partial (o, lse) for the log-sum-exp merge.
+// are zero and discarded, as the Ascend page pads 12 -> 16 heads).  The prologue
+// turns the selection into a per-slot table of K/V row indices in LDS (-1 for a
+// masked slot).  A wave then takes 16 selected tokens at a time:
+//   S^T[token][head] = K . Q^T   8 x v_mfma_f32_16x16x32_bf16; MFMA m covers dims
+//                                32m..32m+31, lane (r, q) giving dims 32m + 8q..+7
+//                                of token r, so each load instruction reads 64
+//                                contiguous bytes of each of the 16 K rows
+//   online softmax in fp32, base 2 (x * scale * log2 e), with a lazy reference
+//                                max: O and l are rescaled only when a head's
+//                                max grows by more than 2^8, so P <= 256
+//   O[head][dim] += P . V        16 x v_mfma_f32_16x16x16bf16_1k (P rounded to
+//                                bf16; lane (c, q) reads dims 8c..8c+7 and
+//                                128+8c..128+8c+7 of the V rows of tokens
+//                                4q..4q+3 -- 256 contiguous bytes per 16 lanes --
+//                                and output tile n takes dim 128 (n / 8) + 8c +
+//                                n % 8)
+// All K and V loads of a tile are issued before the first wait.  The 4 waves'
+// (m, l, O) are merged in LDS and written as the final bf16 output or as an fp32
+// partial (o, lse) for the log-sum-exp merge.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -29,6 +36,11 @@ namespace qsa {
 
 constexpr int kAttnWaves = 4;
 constexpr int kMaxSel = 2048;
+constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
+constexpr int kKRow = kHeadDim + 8;   // padded K row in the LDS tile (elements): spreads rows over banks
+constexpr int kKTile = 16 * kKRow;    // one wave's K tile (elements)
+
+typedef short bf16x4s __attribute__((ext_vector_type(4)));
 
 struct AttnParams {
     const uint16_t* k;
@@ -46,6 +58,8 @@ struct AttnParams {
     int kstride;
     float scale_log2;
     int S;
+    int blocked;  // 1: split s takes a contiguous range of selected blocks; 0: token slots p mod S
+    int table_words;  // int32 words of LDS reserved for the slot table
     uint16_t* out;
     int64_t out_stride;
     float* lse;
@@ -53,18 +67,18 @@ struct AttnParams {
     float* part_lse;
 };
 
-__device__ __forceinline__ uint32_t word_of(const uint4& a, const uint4& b, int e) {
-    // dword e (0..7) of the 32-byte pair (a, b)
-    const uint4& src = e < 4 ? a : b;
-    const int w = e & 3;
-    return w == 0 ? src.x : (w == 1 ? src.y : (w == 2 ? src.z : src.w));
+__device__ __forceinline__ uint32_t u4_word(const uint4& a, int w) {
+    return w == 0 ? a.x : (w == 1 ? a.y : (w == 2 ? a.z : a.w));
 }
 
-__global__ __launch_bounds__(256) void attn_kernel(const AttnParams P) {
-    __shared__ float smem[kAttnWaves * 16 * kHeadDim];  // 64 KiB; first 10 KiB double as token tables
+// Dynamic LDS: the slot table (16 B per selected block of this workgroup) and the
+// 4 waves' K staging tiles (16 padded rows each), later reused for the waves' O
+// exchange (4 waves x g heads x 1 KiB); the launch sizes it to the larger need.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(const AttnParams P) {
+    extern __shared__ float smem[];
     __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
-    int32_t* tok_base = reinterpret_cast<int32_t*>(smem);               // [kMaxSel]
-    uint8_t* tok_nv = reinterpret_cast<uint8_t*>(smem + kMaxSel);       // [kMaxSel]
+    int32_t* slot_row = reinterpret_cast<int32_t*>(smem);
+    // the 4 waves' K tiles follow the slot table (P.table_words int32)
 
     const int S = P.S;
     const int unit = blockIdx.x;
@@ -79,171 +93,198 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams P) {
     const int g = P.g;
     const int tid = threadIdx.x;
 
-    int nsel = P.cnt[(int64_t)row * P.Hkv + h];
-    nsel = max(0, min(nsel, P.kstride));
-    const int32_t* sel_row = P.sel + ((int64_t)row * P.Hkv + h) * P.kstride;
-    for (int j = tid; j < nsel; j += 256) {
-        const int b = sel_row[j];
-        const int64_t pos0 = 4 * (int64_t)b;
-        if (b < 0 || pos0 >= lim) {
-            tok_base[j] = 0;
-            tok_nv[j] = 0;
-        } else {
-            tok_base[j] = (int32_t)token_row(P.block_table, seq, P.max_pages, P.Hkv, h, P.lg_ps, pos0);
-            tok_nv[j] = (uint8_t)min(lim - pos0, (int64_t)4);
-        }
-    }
-    __syncthreads();
-
-    const int ntok = 4 * nsel;                                   // token slots of the selection
-    const int n_s = ntok > s ? (ntok - s + S - 1) / S : 0;      // slots of this split
-    const int ntiles = (n_s + 31) / 32;
-
     const int lane = tid & 63;
     const int wave = wave_id();
     const int c = lane & 15;
     const int qq = lane >> 4;
 
+    // The query, the count and the selection are independent reads: issue them
+    // together.  Blocked splits cut the k selection slots (not the count), so the
+    // selection reads need not wait for the count.
     bf16x8 qb[8];
-    if (c < g) {
-        const uint16_t* qp = P.q + (int64_t)row * P.q_stride + (int64_t)(h * g + c) * kHeadDim + 64 * qq;
+    {
+        const uint16_t* qp = P.q + (int64_t)row * P.q_stride + (int64_t)(h * g + min(c, g - 1)) * kHeadDim + 8 * qq;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
-    } else {
+        for (int m = 0; m < 8; ++m) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 32 * m);
+        if (c >= g) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) qb[m] = bf16x8{};
+            for (int m = 0; m < 8; ++m) qb[m] = bf16x8{};
+        }
     }
+    const int cnt_raw = P.cnt[(int64_t)row * P.Hkv + h];
+    int jb = 0, jcap = P.kstride;
+    if (P.blocked) {
+        const int per = (P.kstride + S - 1) / S;
+        jb = min(P.kstride, s * per);
+        jcap = min(P.kstride, jb + per);
+    }
+    const int32_t* sel_row = P.sel + ((int64_t)row * P.Hkv + h) * P.kstride;
+    constexpr int kIt = kMaxSel / 256;
+    int bsel[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int j = jb + tid + 256 * it;
+        bsel[it] = j < jcap ? sel_row[j] : -1;
+    }
+    // selected blocks [jb, je) feed this workgroup; the table holds their slots
+    const int nsel = max(0, min(cnt_raw, P.kstride));
+    const int je = max(jb, min(nsel, jcap));
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int j = jb + tid + 256 * it;
+        if (j >= je) break;
+        const int b = bsel[it];
+        const int64_t pos0 = 4 * (int64_t)b;
+        int32_t base = 0;
+        int nv = 0;
+        if (b >= 0 && pos0 < lim) {
+            base = (int32_t)token_row(P.block_table, seq, P.max_pages, P.Hkv, h, P.lg_ps, pos0);
+            nv = (int)min(lim - pos0, (int64_t)4);
+        }
+        *reinterpret_cast<int4*>(slot_row + 4 * (j - jb)) = make_int4(
+            nv > 0 ? base : -1, nv > 1 ? base + 1 : -1, nv > 2 ? base + 2 : -1, nv > 3 ? base + 3 : -1);
+    }
+    __syncthreads();
 
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    // split-local slot n lives at table entry slot0 + sstep * n
+    const int ntok = 4 * (je - jb);
+    int n_s, slot0, sstep;
+    if (P.blocked) {
+        n_s = ntok;
+        slot0 = 0;
+        sstep = 1;
+    } else {
+        n_s = ntok > s ? (ntok - s + S - 1) / S : 0;
+        slot0 = s;
+        sstep = S;
+    }
+    const int ntiles = (n_s + 15) / 16;
+    uint16_t* ktile = reinterpret_cast<uint16_t*>(smem + P.table_words) + wave * kKTile;
+
+    float m_run = -INFINITY;  // reference max of head c (log2 units), same in every qq group
+    float l_run = 0.f;        // this lane's share of the head's normaliser
     floatx4 O[16];
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
-        const int n0 = tile * 32;
-        // ---- K rows of tokens 16 th + c (A operand)
-        bf16x8 kb[2][8];
+        const int n0 = tile * 16;
+        // slot -> row; slots past this split's end read as masked
+        int rv[4];
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
-            const int n = n0 + 16 * th + c;
-            const int p = s + S * n;
-            const bool valid = n < n_s && (p & 3) < tok_nv[p >> 2];
-            if (valid) {
-                const uint16_t* kp = P.k + (int64_t)(tok_base[p >> 2] + (p & 3)) * kHeadDim + 64 * qq;
-#pragma unroll
-                for (int m = 0; m < 8; ++m) kb[th][m] = *reinterpret_cast<const bf16x8*>(kp + 8 * m);
-            } else {
-#pragma unroll
-                for (int m = 0; m < 8; ++m) kb[th][m] = bf16x8{};
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int nvv = n0 + 4 * qq + i;
+            rv[i] = nvv < n_s ? slot_row[slot0 + sstep * nvv] : -1;
         }
-        // ---- V rows of tokens 16 th + 4 qq + i, dims 16c .. 16c+15 (B operand)
-        uint4 vv[2][4][2];
-        bool vok[2][4];
+        // ---- issue every load of the tile.  K is read coalesced -- instruction j
+        // covers the 1 KiB of rows 2j and 2j+1 -- and staged through this wave's
+        // LDS tile, from which the MFMA layout is read back.
+        uint4 kraw[8];
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = n0 + 16 * th + 4 * qq + i;
-                const int p = s + S * n;
-                const bool valid = n < n_s && (p & 3) < tok_nv[p >> 2];
-                vok[th][i] = valid;
-                if (valid) {
-                    const uint4* vp = reinterpret_cast<const uint4*>(
-                        P.v + (int64_t)(tok_base[p >> 2] + (p & 3)) * kHeadDim + 16 * c);
-                    vv[th][i][0] = vp[0];
-                    vv[th][i][1] = vp[1];
-                } else {
-                    vv[th][i][0] = make_uint4(0, 0, 0, 0);
-                    vv[th][i][1] = make_uint4(0, 0, 0, 0);
-                }
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int rl = 2 * j + (lane >> 5);  // tile row this lane loads
+            const int nr = n0 + rl;
+            const int rr = nr < n_s ? slot_row[slot0 + sstep * nr] : -1;
+            kraw[j] = *reinterpret_cast<const uint4*>(P.k + (int64_t)max(rr, 0) * kHeadDim + 8 * (lane & 31));
         }
-        // ---- S^T = K . Q^T: st[th][i] = S[head c][token 16 th + 4 qq + i]
-        floatx4 st[2];
+        uint4 vv[4][2];
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
-            st[th] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < 8; ++m) st[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[th][m], qb[m], st[th], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t* vp = P.v + (int64_t)max(rv[i], 0) * kHeadDim + 8 * c;
+            vv[i][0] = *reinterpret_cast<const uint4*>(vp);
+            vv[i][1] = *reinterpret_cast<const uint4*>(vp + 128);
         }
-        // ---- online softmax (base 2)
-        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<uint4*>(ktile + (2 * j + (lane >> 5)) * kKRow + 8 * (lane & 31)) = kraw[j];
+        bf16x8 kb[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) kb[m] = *reinterpret_cast<const bf16x8*>(ktile + c * kKRow + 32 * m + 8 * qq);
+        // ---- S^T = K . Q^T: st[i] = S[head c][token n0 + 4 qq + i]
+        floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[m], qb[m], st, 0, 0, 0);
+        float x[4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[4 * th + i] = vok[th][i] ? st[th][i] * P.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[4 * th + i]);
-            }
+        for (int i = 0; i < 4; ++i) {
+            x[i] = rv[i] >= 0 ? st[i] * P.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, x[i]);
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        uint32_t pb[4];
+        // ---- lazy rescale: only when some head's max passes its reference by 2^8
+        if (__ballot(mx > m_run + kLazy)) {
+            const float m_new = mx > m_run + kLazy ? fmaxf(m_run, mx) : m_run;
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a_i = __shfl(alpha, 4 * qq + i);
+#pragma unroll
+                for (int nt = 0; nt < 16; ++nt) O[nt][i] *= a_i;
+            }
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        uint32_t pw[2];
         float psum = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < 2; ++w) {
             const uint32_t lo = f32_to_bf16_rne(__builtin_amdgcn_exp2f(x[2 * w] - m_use));
             const uint32_t hi = f32_to_bf16_rne(__builtin_amdgcn_exp2f(x[2 * w + 1] - m_use));
             psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
-            pb[w] = lo | (hi << 16);
+            pw[w] = lo | (hi << 16);
         }
-        l_run = l_run * alpha + psum;
+        l_run += psum;
+        // ---- zero the V of masked slots (their weight is 0, their bytes may be anything)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float a_i = __shfl(alpha, 4 * qq + i);
-#pragma unroll
-            for (int nt = 0; nt < 16; ++nt) O[nt][i] *= a_i;
-        }
-        // ---- O += P . V; k-slot 4 th + i of lane (., qq) is token 16 th + 4 qq + i
-        bf16x8 pa;
+        for (int i = 0; i < 4; ++i)
+            if (rv[i] < 0) {
+                vv[i][0] = make_uint4(0, 0, 0, 0);
+                vv[i][1] = make_uint4(0, 0, 0, 0);
+            }
+        // ---- O += P . V; k-slot i of lane (., qq) is token n0 + 4 qq + i
+        bf16x4s pa;
         {
-            uint32_t* pw = reinterpret_cast<uint32_t*>(&pa);
-            pw[0] = pb[0];
-            pw[1] = pb[1];
-            pw[2] = pb[2];
-            pw[3] = pb[3];
+            uint32_t* p32 = reinterpret_cast<uint32_t*>(&pa);
+            p32[0] = pw[0];
+            p32[1] = pw[1];
         }
 #pragma unroll
         for (int nt = 0; nt < 16; ++nt) {
-            const int e = nt >> 1;
-            uint32_t bw[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int th = w >> 1;
-                const int i0 = 2 * (w & 1);
-                const uint32_t d0 = word_of(vv[th][i0][0], vv[th][i0][1], e);
-                const uint32_t d1 = word_of(vv[th][i0 + 1][0], vv[th][i0 + 1][1], e);
-                bw[w] = (nt & 1) ? ((d0 >> 16) | (d1 & 0xffff0000u)) : ((d0 & 0xffffu) | (d1 << 16));
+            const int hf = nt >> 3, e = (nt & 7) >> 1;  // dim 128 hf + 8c + (nt & 7): dword e of half hf
+            const uint32_t d0 = u4_word(vv[0][hf], e), d1 = u4_word(vv[1][hf], e);
+            const uint32_t d2 = u4_word(vv[2][hf], e), d3 = u4_word(vv[3][hf], e);
+            bf16x4s vb;
+            uint32_t* v32 = reinterpret_cast<uint32_t*>(&vb);
+            if (nt & 1) {
+                v32[0] = (d0 >> 16) | (d1 & 0xffff0000u);
+                v32[1] = (d2 >> 16) | (d3 & 0xffff0000u);
+            } else {
+                v32[0] = (d0 & 0xffffu) | (d1 << 16);
+                v32[1] = (d2 & 0xffffu) | (d3 << 16);
             }
-            bf16x8 vb;
-            uint32_t* vw = reinterpret_cast<uint32_t*>(&vb);
-            vw[0] = bw[0];
-            vw[1] = bw[1];
-            vw[2] = bw[2];
-            vw[3] = bw[3];
-            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[nt], 0, 0, 0);
+            O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nt], 0, 0, 0);
         }
     }
 
     // ---- merge the 4 waves in LDS
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    __syncthreads();  // token tables are dead; smem becomes the O exchange
+    __syncthreads();  // the slot table is dead; smem becomes the O exchange
     if (qq == 0) {
         wm[wave][c] = m_run;
         wl[wave][c] = l_tot;
     }
-    float* ow = smem + wave * 16 * kHeadDim;
+    float* ow = smem + wave * g * kHeadDim;
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt)
+    for (int i = 0; i < 4; ++i)
+        if (4 * qq + i < g) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ow[(4 * qq + i) * kHeadDim + 16 * c + nt] = O[nt][i];
+            for (int nt = 0; nt < 16; ++nt)
+                ow[(4 * qq + i) * kHeadDim + 128 * (nt >> 3) + 8 * c + (nt & 7)] = O[nt][i];
+        }
     __syncthreads();
 
     const float kLn2 = 0.6931471805599453f;
@@ -252,14 +293,15 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams P) {
         const int d = e & (kHeadDim - 1);
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wm[w][hh]);
+        for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wl[w][hh] > 0.f ? wm[w][hh] : -INFINITY);
         float o = 0.f, lse_v = -INFINITY;
         if (M != -INFINITY) {
             float num = 0.f, den = 0.f;
 #pragma unroll
             for (int w = 0; w < kAttnWaves; ++w) {
+                if (!(wl[w][hh] > 0.f)) continue;
                 const float f = __builtin_amdgcn_exp2f(wm[w][hh] - M);
-                num += f * smem[(w * 16 + hh) * kHeadDim + d];
+                num += f * smem[(w * g + hh) * kHeadDim + d];
                 den += f * wl[w][hh];
             }
             o = num / den;
@@ -278,7 +320,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams P) {
 }
 
 hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt, int k,
-                       float scale, int num_splits, const AttnOut& o, hipStream_t st) {
+                       float scale, int num_splits, bool blocked, const AttnOut& o, hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
     AttnParams P;
     P.k = kv.k;
@@ -300,13 +342,19 @@ hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_i
     P.kstride = k;
     P.scale_log2 = scale * 1.4426950408889634f;
     P.S = num_splits;
+    P.blocked = blocked ? 1 : 0;
     P.out = o.out;
     P.out_stride = o.out_stride;
     P.lse = o.lse;
     P.part_out = o.part_out;
     P.part_lse = o.part_lse;
     const int64_t nblocks = (int64_t)rows.R * kv.Hkv * num_splits;
-    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)nblocks), dim3(256), 0, st, P);
+    const int blocks_per_wg = num_splits > 1 && blocked ? (k + num_splits - 1) / num_splits : k;
+    P.table_words = 4 * ((blocks_per_wg + 3) & ~3);  // keeps the K tiles 16-byte aligned
+    const size_t loop = (size_t)P.table_words * 4 + (size_t)kAttnWaves * kKTile * sizeof(uint16_t);
+    const size_t xchg = (size_t)kAttnWaves * P.g * kHeadDim * sizeof(float);
+    const size_t lds = loop > xchg ? loop : xchg;
+    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)nblocks), dim3(256), lds, st, P);
     return hipGetLastError();
 }
 

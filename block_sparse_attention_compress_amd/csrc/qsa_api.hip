@@ -98,9 +98,9 @@ int check_q(const void* q, int64_t q_row_stride, int Hq) {
 }
 
 int auto_splits(int64_t units, int k) {
-    // aim at ~1024 workgroups (4 per CU) while keeping >= 32 token slots per wave
-    int64_t s = (1024 + units - 1) / (units > 0 ? units : 1);
-    const int64_t cap = k / 32 > 1 ? k / 32 : 1;
+    // aim at ~512 workgroups (2 resident per CU) while keeping >= 16 blocks per split
+    int64_t s = (512 + units - 1) / (units > 0 ? units : 1);
+    const int64_t cap = k / 16 > 1 ? k / 16 : 1;
     if (s > cap) s = cap;
     if (s > 16) s = 16;
     return s < 1 ? 1 : (int)s;
@@ -196,7 +196,7 @@ int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
         if (!part_lse) return fail(QSA_ERR_INVALID_ARG, "part_lse is NULL");
         if (!aligned(part_out, 16)) return fail(QSA_ERR_INVALID_ARG, "part_out must be 16-byte aligned");
         qsa::AttnOut o{nullptr, 0, nullptr, part_out, part_lse};
-        return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, num_splits, o, st),
+        return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, num_splits, false, o, st),
                           "qsa_sparse_attn_decode");
     }
     if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
@@ -205,7 +205,7 @@ int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
     const int S = num_splits == 0 ? auto_splits((int64_t)p.batch * p.Hkv, k) : num_splits;
     if (S == 1) {
         qsa::AttnOut o{static_cast<uint16_t*>(out), out_row_stride, lse, nullptr, nullptr};
-        return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, o, st), "qsa_sparse_attn_decode");
+        return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, false, o, st), "qsa_sparse_attn_decode");
     }
     if (out_row_stride != (int64_t)Hq * QSA_HEAD_DIM || !aligned(out, 8))
         return fail(QSA_ERR_UNSUPPORTED, "a split decode writes a dense, 8-byte aligned out");
@@ -218,7 +218,7 @@ int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
     float* wl = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          (((size_t)n * QSA_HEAD_DIM * sizeof(float) + 255) & ~(size_t)255));
     qsa::AttnOut o{nullptr, 0, nullptr, wo, wl};
-    if (int rc = hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, S, o, st), "qsa_sparse_attn_decode"))
+    if (int rc = hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, S, true, o, st), "qsa_sparse_attn_decode"))
         return rc;
     return hip_status(qsa::launch_merge(wo, wl, S, p.batch * Hq, QSA_HEAD_DIM, static_cast<uint16_t*>(out), lse, st),
                       "qsa_sparse_attn_decode (merge)");
@@ -243,7 +243,7 @@ int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
     const float sc = scale > 0.f ? scale : 0.0625f;
     qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, q_seq, q_pos, R, Hq};
     qsa::AttnOut o{static_cast<uint16_t*>(out), out_row_stride, lse, nullptr, nullptr};
-    return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, o, static_cast<hipStream_t>(stream)),
+    return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, false, o, static_cast<hipStream_t>(stream)),
                       "qsa_sparse_attn_extend");
 }
 

@@ -44,8 +44,11 @@ struct AttnOut {
     float* part_lse;          // fp32 [S][R][Hq]
 };
 
+// num_splits work units per (row, KV head); blocked: split s takes the
+// contiguous range [s, s+1) * ceil(k / S) of the k selection slots, else the
+// token slots p with p mod S == s
 hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt, int k,
-                       float scale, int num_splits, const AttnOut& o, hipStream_t st);
+                       float scale, int num_splits, bool blocked, const AttnOut& o, hipStream_t st);
 
 hipError_t launch_merge(const float* part_out, const float* part_lse, int S, int N, int D, uint16_t* out,
                         float* out_lse, hipStream_t st);

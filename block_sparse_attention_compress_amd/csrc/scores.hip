@@ -23,6 +23,11 @@ namespace qsa {
 
 constexpr int kStreamChunk = 256;  // blocks per workgroup (4 waves x 64)
 
+// PAGE16: a page holds >= 16 blocks (page_size >= 64).  A wave's group of 16
+// blocks starts 16-aligned, so it lies in one page: one block-table lookup gives
+// 16 KiB of contiguous block keys, and the loads need no per-block branch (slots
+// past the row end are still inside the page; their sums are never written).
+template <bool PAGE16>
 __global__ __launch_bounds__(256) void scores_stream_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int g, const float* __restrict__ ckey, const int32_t* __restrict__ block_table,
@@ -39,41 +44,71 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
     if (chunk0 >= n_elig) return;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
-
-    // group-summed query: lane holds dims 4*lane .. 4*lane+3
-    float4 qs = make_float4(0.f, 0.f, 0.f, 0.f);
-    const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + 4 * lane;
-    for (int j = 0; j < g; ++j) {
-        const uint2 w = *reinterpret_cast<const uint2*>(qrow + j * kHeadDim);
-        qs.x += bf16_lo(w.x);
-        qs.y += bf16_hi(w.x);
-        qs.z += bf16_lo(w.y);
-        qs.w += bf16_hi(w.y);
-    }
+    const int wb0 = chunk0 + wave * 64;  // this wave's first block
+    if (wb0 >= n_elig) return;
 
     const int lg_bpp = lg_ps - 2;  // blocks per page = page_size / 4
-    float* srow = scores + ((int64_t)row * Hkv + h) * score_stride;
-    for (int grp = 0; grp < 4; ++grp) {
-        const int b0 = chunk0 + wave * 64 + grp * 16;
-        if (b0 >= n_elig) break;
-        float4 v[16];
+    const int32_t* bt = block_table + (int64_t)seq * max_pages;
+    // block-key rows of the wave's 4 groups (PAGE16), looked up before any wait
+    int64_t gbase[4];
+    if (PAGE16) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int b = b0 + j;
-            if (b < n_elig) {
-                const int64_t page = block_table[(int64_t)seq * max_pages + (b >> lg_bpp)];
+        for (int grp = 0; grp < 4; ++grp) {
+            const int b0 = min(wb0 + grp * 16, n_elig - 1) & ~15;
+            gbase[grp] = (((int64_t)bt[b0 >> lg_bpp] * Hkv + h) << lg_bpp) + (b0 & ((1 << lg_bpp) - 1));
+        }
+    }
+
+    auto load_group = [&](int grp, float4* v) {
+        const int b0 = wb0 + grp * 16;
+        if (PAGE16) {
+            const float* src = ckey + gbase[grp] * kHeadDim + 4 * lane;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = *reinterpret_cast<const float4*>(src + j * kHeadDim);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int b = min(b0 + j, n_elig - 1);
+                const int64_t page = bt[b >> lg_bpp];
                 const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
                 v[j] = *reinterpret_cast<const float4*>(ckey + brow * kHeadDim + 4 * lane);
-            } else {
-                v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
+    };
+    // the first group's block keys are requested before the query
+    float4 v[16];
+    load_group(0, v);
+
+    // group-summed query: lane holds dims 4*lane .. 4*lane+3; the g loads are
+    // issued together (one wait), summed in head order
+    float4 qs = make_float4(0.f, 0.f, 0.f, 0.f);
+    {
+        const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + 4 * lane;
+        uint2 qw[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qw[j] = j < g ? *reinterpret_cast<const uint2*>(qrow + j * kHeadDim) : make_uint2(0, 0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            qs.x += bf16_lo(qw[j].x);
+            qs.y += bf16_hi(qw[j].x);
+            qs.z += bf16_lo(qw[j].y);
+            qs.w += bf16_hi(qw[j].y);
+        }
+    }
+
+    float* srow = scores + ((int64_t)row * Hkv + h) * score_stride;
+    for (int grp = 0; grp < 4; ++grp) {
+        const int b0 = wb0 + grp * 16;
+        if (b0 >= n_elig) break;
         float p[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) p[j] = qs.x * v[j].x + qs.y * v[j].y + qs.z * v[j].z + qs.w * v[j].w;
+        // the next group's loads fly while this group is reduced
+        if (grp < 3 && b0 + 16 < n_elig) load_group(grp + 1, v);
         // reduce-scatter: after the step across lane bit m (m = 5, 4, 3, 2) a lane
         // keeps the half of its blocks selected by that bit; finally lane l holds
-        // the full sum of block l >> 2 (lanes differing in bits 0, 1 agree).
+        // the full sum of block l >> 2 (lanes differing in bits 0, 1 agree).  Each
+        // block's partial sums only ever meet each other.
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const bool up = lane & 32;
@@ -133,9 +168,12 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
         const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + 64 * kq;
         for (int j = 0; j < g; ++j) {
             const uint4* p = reinterpret_cast<const uint4*>(qrow + j * kHeadDim);
+            uint4 ws[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ws[i] = p[i];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint4 w = p[i];
+                const uint4 w = ws[i];
                 a[8 * i + 0] += bf16_lo(w.x);
                 a[8 * i + 1] += bf16_hi(w.x);
                 a[8 * i + 2] += bf16_lo(w.y);
@@ -197,9 +235,14 @@ hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scor
                                 hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
     dim3 grid((score_stride + kStreamChunk - 1) / kStreamChunk, kv.Hkv, rows.R);
-    hipLaunchKernelGGL(scores_stream_kernel, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq, rows.q_pos,
-                       rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps, kv.max_pages, scores,
-                       score_stride);
+    if (kv.lg_ps >= 6)
+        hipLaunchKernelGGL(scores_stream_kernel<true>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,
+                           rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,
+                           kv.max_pages, scores, score_stride);
+    else
+        hipLaunchKernelGGL(scores_stream_kernel<false>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,
+                           rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,
+                           kv.max_pages, scores, score_stride);
     return hipGetLastError();
 }
 

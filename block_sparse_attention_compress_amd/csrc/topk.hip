@@ -5,91 +5,364 @@
 // verandert").  Ties are not discussed on the pages; the order used here is
 // (score descending, block index ascending), with -0 equal to +0.
 //
-// One 512-thread workgroup per (row, KV head).  Scores are mapped to
-// order-preserving uint32 keys; three radix passes (11, 11 and 10 bits) with
-// LDS histograms find the exact k-th key T and how many of the keys equal to T
-// are needed.  A final ordered pass writes the blocks with key > T and the
-// lowest-indexed blocks with key == T, in ascending block order (so the output is
-// the same whatever the thread timing).  The row is re-read from L2 per pass.
+// Both kernels find the exact k-th largest key T (order-preserving uint32 map of
+// the fp32 score) and how many keys equal to T are needed, then write, in
+// ascending block order, every block with key > T and the lowest-indexed blocks
+// with key == T.  The result does not depend on thread timing.
+//
+// topk_reg_kernel (rows of up to 65,536 blocks): one 1024-thread workgroup per
+// (row, KV head); the row lives in registers (KPT scores per thread, block
+// t + 1024 j in thread t).  Radix digits of raw float keys crowd into a few
+// exponent bins, and LDS atomics on one address serialise, so the first pass
+// bins uniformly between the row's min and max instead: any monotonic binning
+// keeps the selection exact.  The bin holding the k-th value is then resolved
+// exactly -- by ranking its candidates directly when there are at most 1024 of
+// them, else by exact radix passes restricted to that bin.
+//
+// topk_global_kernel (longer rows): the same select with exact radix passes
+// (11, 11, 10 bits) re-reading the row from L2.
+#include <float.h>
+
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
 namespace qsa {
 
-constexpr int kTopkThreads = 512;
-constexpr int kTopkWaves = kTopkThreads / 64;
-
-// Inclusive scan over the block of one int per thread, in reverse thread order
-// (thread t gets the sum over threads >= t).  Uses `tmp` [kTopkWaves].
+// Suffix sum over the block (thread t gets the sum over threads >= t) of one
+// int per thread.  tmp holds NW ints.
+template <int NW>
 __device__ __forceinline__ int block_suffix_sum(int v, int* tmp) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    // within a wave: suffix over lanes >= lane
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int other = __shfl_down(v, o);
         if (lane + o < 64) v += other;
     }
-    if (lane == 0) tmp[wave] = v;  // wave total
+    if (lane == 0) tmp[wave] = v;
     __syncthreads();
     int after = 0;
-    for (int w = wave + 1; w < kTopkWaves; ++w) after += tmp[w];
+    for (int w = wave + 1; w < NW; ++w) after += tmp[w];
     __syncthreads();
     return v + after;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int score_stride,
-                                                            const int32_t* __restrict__ q_pos, int Hkv, int k,
-                                                            int32_t* __restrict__ sel_idx,
-                                                            int32_t* __restrict__ sel_cnt) {
-    __shared__ int hist[2048];
-    __shared__ int tmp[kTopkWaves];
-    __shared__ int found_bin, found_above;
-    __shared__ int wave_gt[kTopkWaves], wave_eq[kTopkWaves];
+// Exclusive prefix sum over the block (thread order) of two ints per thread.
+template <int NW>
+__device__ __forceinline__ void block_exclusive_scan2(int& a, int& b, int* tmp) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int ia = a, ib = b;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int pa = __shfl_up(ia, o), pb = __shfl_up(ib, o);
+        if (lane >= o) {
+            ia += pa;
+            ib += pb;
+        }
+    }
+    if (lane == 63) {
+        tmp[wave] = ia;
+        tmp[NW + wave] = ib;
+    }
+    __syncthreads();
+    int ba = 0, bb = 0;
+    for (int w = 0; w < wave; ++w) {
+        ba += tmp[w];
+        bb += tmp[NW + w];
+    }
+    __syncthreads();
+    a = ba + ia - a;
+    b = bb + ib - b;
+}
+
+__device__ __forceinline__ float block_min_max(float& mn, float& mx, float* tmp) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    if (lane == 0) {
+        tmp[wave] = mn;
+        tmp[32 + wave] = mx;
+    }
+    __syncthreads();
+    mn = tmp[0];
+    mx = tmp[32];
+    for (int w = 1; w < nw; ++w) {
+        mn = fminf(mn, tmp[w]);
+        mx = fmaxf(mx, tmp[32 + w]);
+    }
+    __syncthreads();
+    return mx - mn;
+}
+
+// Trivial rows: everything eligible selected (n <= k), or nothing (k == 0).
+__device__ __forceinline__ bool topk_trivial(int n, int k, int32_t* out, int32_t* cnt_out) {
+    if (n <= k) {
+        for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = j < n ? j : -1;
+        if (threadIdx.x == 0) *cnt_out = n;
+        return true;
+    }
+    if (k == 0) {
+        if (threadIdx.x == 0) *cnt_out = 0;
+        return true;
+    }
+    return false;
+}
+
+__device__ __forceinline__ int eligible(const int32_t* q_pos, int row, int score_stride) {
+    if (!q_pos) return score_stride;
+    const int t = q_pos[row];
+    return t < 0 ? 0 : min(t / 4 + 1, score_stride);
+}
+
+// ------------------------------------------------------------------ registers
+
+constexpr int kRegThreads = 1024;
+constexpr int kRegWaves = kRegThreads / 64;
+constexpr int kBins = 2048;
+
+// KPT scores per thread: the first KR in registers, the rest in LDS (a 65,536-block
+// row would not fit 1024 threads x 128 registers).
+template <int KPT, int KR>
+__global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __restrict__ scores, int score_stride,
+                                                               const int32_t* __restrict__ q_pos, int Hkv, int k,
+                                                               int32_t* __restrict__ sel_idx,
+                                                               int32_t* __restrict__ sel_cnt) {
+    __shared__ int hist[kBins];
+    __shared__ float cand_val[kRegThreads];
+    __shared__ int cand_idx[kRegThreads];
+    __shared__ int cnt_gt[KPT * kRegWaves], cnt_eq[KPT * kRegWaves];
+    __shared__ int itmp[2 * kRegWaves];
+    __shared__ float ftmp[64];
+    __shared__ int sh_bin, sh_above, sh_ncand, sh_need_eq;
+    __shared__ uint32_t sh_T;
+    constexpr int KL = KPT - KR;
+    __shared__ float vl[KL > 0 ? KL * kRegThreads : 1];
 
     const int unit = blockIdx.x;
-    const int row = unit / Hkv;
-    int n = score_stride;
-    if (q_pos) {
-        const int t = q_pos[row];
-        n = t < 0 ? 0 : min(t / 4 + 1, score_stride);
+    const int n = eligible(q_pos, unit / Hkv, score_stride);
+    int32_t* out = sel_idx + (int64_t)unit * k;
+    if (topk_trivial(n, k, out, sel_cnt + unit)) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const float* s = scores + (int64_t)unit * score_stride;
+    // slots past n hold -inf (scores are finite): it is never selected, and
+    // every test below stays a function of the value (no per-slot masks kept live)
+    float v[KR];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int i = tid + kRegThreads * j;
+        // unconditional (clamped) loads, so all KPT are in flight at once
+        const float raw = s[min(i, n - 1)];
+        const float x = i < n ? raw + 0.0f : -INFINITY;  // + 0 turns -0 into +0
+        if (j < KR) v[j < KR ? j : 0] = x;
+        else vl[(j - KR) * kRegThreads + tid] = x;
     }
+    auto V = [&](int j) -> float { return j < KR ? v[j < KR ? j : 0] : vl[(j - KR) * kRegThreads + tid]; };
+    float mn = FLT_MAX, mx = -FLT_MAX;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        mn = fminf(mn, V(j) == -INFINITY ? FLT_MAX : V(j));
+        mx = fmaxf(mx, V(j));
+    }
+    const float range = block_min_max(mn, mx, ftmp);
+    if (range == 0.f) {  // every score equal: the k lowest indices
+        for (int j = tid; j < k; j += kRegThreads) out[j] = j;
+        if (tid == 0) sel_cnt[unit] = k;
+        return;
+    }
+    float scale = (float)kBins / range;
+    if (!(scale <= FLT_MAX)) scale = FLT_MAX;
+    // monotonic in x; the -inf padding lands in bin 0 below every real score
+    auto bin_of = [&](float x) { return (int)fminf(fmaxf((x - mn) * scale, 0.f), (float)(kBins - 1)); };
+
+    // ---- pass 1: uniform bins over [mn, mx]
+    for (int i = tid; i < kBins; i += kRegThreads) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (V(j) != -INFINITY) atomicAdd(&hist[bin_of(V(j))], 1);
+    __syncthreads();
+    {
+        const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+        const int incl = block_suffix_sum<kRegWaves>(h0 + h1, itmp);
+        const int above = incl - h0 - h1;
+        if (above < k && k <= incl) {
+            if (above + h1 >= k) {
+                sh_bin = 2 * tid + 1;
+                sh_above = above;
+            } else {
+                sh_bin = 2 * tid;
+                sh_above = above + h1;
+            }
+        }
+        if (tid == 0) sh_ncand = 0;
+        __syncthreads();
+    }
+    const int B = sh_bin;
+    const int need = k - sh_above;  // how many of bin B's elements are taken (>= 1)
+    const int m = hist[B];
+
+    if (m <= kRegThreads) {
+        // ---- rank the bin's candidates directly
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (V(j) != -INFINITY && bin_of(V(j)) == B) {
+                const int slot = atomicAdd(&sh_ncand, 1);
+                cand_val[slot] = V(j);
+                cand_idx[slot] = tid + kRegThreads * j;
+            }
+        }
+        __syncthreads();
+        if (tid < m) {
+            const float x = cand_val[tid];
+            const int xi = cand_idx[tid];
+            int rank = 0, gt = 0;
+            for (int u = 0; u < m; ++u) {
+                const float y = cand_val[u];
+                gt += y > x;
+                rank += (y > x) || (y == x && cand_idx[u] < xi);
+            }
+            if (rank == need - 1) {  // the k-th element overall
+                sh_T = order_key(x);
+                sh_need_eq = need - gt;
+            }
+        }
+        __syncthreads();
+    } else {
+        // ---- crowded bin: exact radix passes over the keys of bin B
+        uint32_t prefix = 0, mask = 0;
+        int remaining = need;
+        const int shifts[3] = {21, 10, 0};
+        const int widths[3] = {11, 11, 10};
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = shifts[pass];
+            const int nb = 1 << widths[pass];
+            for (int i = tid; i < kBins; i += kRegThreads) hist[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const uint32_t key = order_key(V(j));
+                if (V(j) != -INFINITY && bin_of(V(j)) == B && (key & mask) == prefix)
+                    atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
+            }
+            __syncthreads();
+            const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+            const int incl = block_suffix_sum<kRegWaves>(h0 + h1, itmp);
+            const int above = incl - h0 - h1;
+            if (above < remaining && remaining <= incl) {
+                if (above + h1 >= remaining) {
+                    sh_bin = 2 * tid + 1;
+                    sh_above = above;
+                } else {
+                    sh_bin = 2 * tid;
+                    sh_above = above + h1;
+                }
+            }
+            __syncthreads();
+            remaining -= sh_above;
+            prefix |= (uint32_t)sh_bin << shift;
+            mask |= (uint32_t)(nb - 1) << shift;
+            __syncthreads();
+        }
+        if (tid == 0) {
+            sh_T = prefix;
+            sh_need_eq = remaining;
+        }
+        __syncthreads();
+    }
+    const uint32_t T = sh_T;
+    const int need_eq = sh_need_eq;
+
+    // ---- ordered compaction: element t + 1024 j comes after all of rows < j and
+    // after the lower threads of row j
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const uint32_t key = order_key(V(j));
+        const uint64_t g = __ballot(key > T);
+        const uint64_t e = __ballot(key == T);
+        if (lane == 0) {
+            cnt_gt[j * kRegWaves + wave] = __popcll(g);
+            cnt_eq[j * kRegWaves + wave] = __popcll(e);
+        }
+    }
+    __syncthreads();
+    {
+        int a = tid < KPT * kRegWaves ? cnt_gt[tid] : 0;
+        int b = tid < KPT * kRegWaves ? cnt_eq[tid] : 0;
+        block_exclusive_scan2<kRegWaves>(a, b, itmp);
+        if (tid < KPT * kRegWaves) {
+            cnt_gt[tid] = a;
+            cnt_eq[tid] = b;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int i = tid + kRegThreads * j;
+        const uint32_t key = order_key(V(j));
+        const bool is_gt = key > T;
+        const bool is_eq = key == T;
+        const uint64_t g = __ballot(is_gt);
+        const uint64_t e = __ballot(is_eq);
+        const int gt_before = cnt_gt[j * kRegWaves + wave] + __popcll(g & below);
+        const int eq_before = cnt_eq[j * kRegWaves + wave] + __popcll(e & below);
+        int pos = -1;
+        if (is_gt) pos = gt_before + min(eq_before, need_eq);
+        if (is_eq && eq_before < need_eq) pos = gt_before + eq_before;
+        if (pos >= 0 && pos < k) out[pos] = i;
+    }
+    if (tid == 0) sel_cnt[unit] = k;
+}
+
+// --------------------------------------------------------------------- global
+
+constexpr int kGlobThreads = 512;
+constexpr int kGlobWaves = kGlobThreads / 64;
+
+__global__ __launch_bounds__(kGlobThreads) void topk_global_kernel(const float* __restrict__ scores, int score_stride,
+                                                                   const int32_t* __restrict__ q_pos, int Hkv, int k,
+                                                                   int32_t* __restrict__ sel_idx,
+                                                                   int32_t* __restrict__ sel_cnt) {
+    __shared__ int hist[2048];
+    __shared__ int tmp[kGlobWaves];
+    __shared__ int found_bin, found_above;
+    __shared__ int wave_gt[kGlobWaves], wave_eq[kGlobWaves];
+
+    const int unit = blockIdx.x;
+    const int n = eligible(q_pos, unit / Hkv, score_stride);
     const float* s = scores + (int64_t)unit * score_stride;
     int32_t* out = sel_idx + (int64_t)unit * k;
     const int tid = threadIdx.x;
+    if (topk_trivial(n, k, out, sel_cnt + unit)) return;
 
-    if (n <= k) {  // everything eligible is selected
-        for (int j = tid; j < k; j += kTopkThreads) out[j] = j < n ? j : -1;
-        if (tid == 0) sel_cnt[unit] = n;
-        return;
-    }
-    if (k == 0) {
-        if (tid == 0) sel_cnt[unit] = 0;
-        return;
-    }
-
-    // ---- radix select of the k-th largest key
     uint32_t prefix = 0, mask = 0;
-    int remaining = k;  // how many still to take among keys matching prefix
+    int remaining = k;
     const int shifts[3] = {21, 10, 0};
     const int widths[3] = {11, 11, 10};
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = shifts[pass];
         const int nbins = 1 << widths[pass];
-        for (int i = tid; i < nbins; i += kTopkThreads) hist[i] = 0;
+        for (int i = tid; i < nbins; i += kGlobThreads) hist[i] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kTopkThreads) {
+        for (int i = tid; i < n; i += kGlobThreads) {
             const uint32_t key = order_key(s[i]);
             if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nbins - 1)], 1);
         }
         __syncthreads();
-        // thread t owns bins [t*per, (t+1)*per); find the bin holding the
-        // remaining-th largest matching key
-        const int per = nbins / kTopkThreads;  // 4, 4, 2
+        const int per = nbins / kGlobThreads;
         int local = 0;
         for (int i = 0; i < per; ++i) local += hist[tid * per + i];
-        const int incl = block_suffix_sum(local, tmp);  // keys in bins >= tid*per
-        const int above = incl - local;                 // keys in bins > my range
+        const int incl = block_suffix_sum<kGlobWaves>(local, tmp);
+        const int above = incl - local;
         if (above < remaining && remaining <= incl) {
             int cum = above;
             for (int b = tid * per + per - 1; b >= tid * per; --b) {
@@ -108,12 +381,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         __syncthreads();
     }
     const uint32_t T = prefix;
-    const int need_eq = remaining;  // >= 1
+    const int need_eq = remaining;
 
-    // ---- ordered compaction: wave w owns a contiguous segment of the row
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int seg = ((n + kTopkWaves * 64 - 1) / (kTopkWaves * 64)) * 64;
+    const int seg = ((n + kGlobWaves * 64 - 1) / (kGlobWaves * 64)) * 64;
     const int lo = wave * seg, hi = min(n, lo + seg);
     int gt = 0, eq = 0;
     for (int base = lo; base < hi; base += 64) {
@@ -151,11 +423,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     if (tid == 0) sel_cnt[unit] = k;
 }
 
+template <int KPT, int KR>
+static void launch_reg(const float* scores, int score_stride, const int32_t* q_pos, int units, int Hkv, int k,
+                       int32_t* sel_idx, int32_t* sel_cnt, hipStream_t st) {
+    hipLaunchKernelGGL((topk_reg_kernel<KPT, KR>), dim3(units), dim3(kRegThreads), 0, st, scores, score_stride, q_pos, Hkv,
+                       k, sel_idx, sel_cnt);
+}
+
 hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,
                        int32_t* sel_idx, int32_t* sel_cnt, hipStream_t st) {
     if (R == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3(R * Hkv), dim3(kTopkThreads), 0, st, scores, score_stride, q_pos, Hkv, k,
-                       sel_idx, sel_cnt);
+    const int units = R * Hkv;
+    const int per = (score_stride + kRegThreads - 1) / kRegThreads;  // scores per thread
+    if (per <= 1) launch_reg<1, 1>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
+    else if (per <= 2) launch_reg<2, 2>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
+    else if (per <= 4) launch_reg<4, 4>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
+    else if (per <= 8) launch_reg<8, 8>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
+    else if (per <= 16) launch_reg<16, 16>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
+    else if (per <= 32) launch_reg<32, 32>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
+    else if (per <= 64) launch_reg<64, 32>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
+    else
+        hipLaunchKernelGGL(topk_global_kernel, dim3(units), dim3(kGlobThreads), 0, st, scores, score_stride, q_pos,
+                           Hkv, k, sel_idx, sel_cnt);
     return hipGetLastError();
 }
 

@@ -93,3 +93,27 @@ def extend_step(kv: KVCache, q: torch.Tensor, q_seq: torch.Tensor, q_pos: torch.
     qsa_topk_blocks(buf.scores, buf.score_stride, q_pos, R, Hkv, buf.k, buf.sel_idx, buf.sel_cnt, stream=stream)
     qsa_sparse_attn_extend(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale, buf.out,
                            buf.out.stride(0), buf.lse, stream=stream)
+
+
+class DecodeGraph:
+    """A decode step captured once in a HIP graph and replayed.
+
+    The library never allocates, synchronises or memsets, so the five launches of
+    a step record as plain kernel nodes.  Inputs are read from the buffers given at
+    capture time: update them in place (q, q_pos, the cache) between replays."""
+
+    def __init__(self, kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: DecodeBuffers, scale: float = 0.0,
+                 num_splits: int = 0, warmup: int = 2):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                decode_step(kv, q, q_pos, buf, scale=scale, num_splits=num_splits)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            decode_step(kv, q, q_pos, buf, scale=scale, num_splits=num_splits)
+        self._keep = (kv, q, q_pos, buf)
+
+    def replay(self) -> None:
+        self.graph.replay()

@@ -147,16 +147,18 @@ QSA_API int qsa_topk_blocks(const float* scores, int32_t score_stride, const int
  * softmax; scale <= 0 selects 1/sqrt(256) = 1/16.  An empty T gives output 0
  * and lse = -inf (fully masked rows keep a zero output, as on the Ascend page).
  *
- * Split-KV: the selected tokens, in order, have ranks p = 0..|T|-1; split s
- * of S takes the tokens with p mod S == s.
- *  - part_out != NULL: num_splits = S >= 1 partials are written,
+ * Split-KV: the selected tokens, in order, have ranks p = 0..|T|-1.
+ *  - part_out != NULL: num_splits = S >= 1 partials are written, split s
+ *    holding the tokens with p mod S == s (interleaved),
  *      part_out fp32 [S][batch][Hq][256] (normalised), part_lse fp32 [S][batch][Hq]
  *    (natural log); out / lse are not touched.  qsa_merge_lse combines them.
  *  - part_out == NULL: the final result is written, out bf16 at
  *    out + row * out_row_stride ([Hq][256] per row), lse fp32 [batch][Hq]
  *    (lse may be NULL).  num_splits = 0 lets the library choose the split
- *    count; any S > 1 is merged internally through `workspace`, which must
- *    hold qsa_decode_workspace_bytes(batch, Hq, num_splits) bytes.
+ *    count; any S > 1 splits the selected blocks into S contiguous ranges
+ *    (the merged result does not depend on the partition) and merges them
+ *    internally through `workspace`, which must hold
+ *    qsa_decode_workspace_bytes(batch, Hq, num_splits) bytes.
  */
 QSA_API int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq,
                            const int32_t* sel_idx, const int32_t* sel_cnt, int32_t k, float scale,
