@@ -38,7 +38,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kMaxSel = 2048;
 constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
 constexpr int kKRow = kHeadDim + 8;   // padded K row in the LDS tile (elements): spreads rows over banks
-constexpr int kKTile = 16 * kKRow;    // one wave's K tile (elements)
+constexpr int kKTile = 16 * kKRow;    // one wave's K (or V) tile (elements)
 
 typedef short bf16x4s __attribute__((ext_vector_type(4)));
 
@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         sstep = S;
     }
     const int ntiles = (n_s + 15) / 16;
-    uint16_t* ktile = reinterpret_cast<uint16_t*>(smem + P.table_words) + wave * kKTile;
+    uint16_t* ktile = reinterpret_cast<uint16_t*>(smem + P.table_words) + wave * 2 * kKTile;
+    uint16_t* vtile = ktile + kKTile;
 
     float m_run = -INFINITY;  // reference max of head c (log2 units), same in every qq group
     float l_run = 0.f;        // this lane's share of the head's normaliser
@@ -167,39 +168,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // Raw tile loads are coalesced -- instruction j covers the 1 KiB of tile rows
+    // 2j and 2j+1 -- and land in this wave's LDS tiles, from which the MFMA
+    // layouts are read.  The loads of tile i+1 are issued before tile i is
+    // computed, so a wave always has a tile in flight.
+    // (the raw tile is 16 named registers, not an array: an array indexed in a
+    // loop across the tile pipeline was kept in scratch memory)
+    uint4 k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+#define QSA_LOAD_J(J, KX, VX)                                                               \
+    do {                                                                                    \
+        const int nr = n0_ + 2 * (J) + (lane >> 5);                                         \
+        const int rr = nr < n_s ? slot_row[slot0 + sstep * nr] : -1;                        \
+        const int64_t off = (int64_t)max(rr, 0) * kHeadDim + 8 * (lane & 31);               \
+        KX = *reinterpret_cast<const uint4*>(P.k + off);                                    \
+        VX = *reinterpret_cast<const uint4*>(P.v + off);                                    \
+    } while (0)
+#define QSA_LOAD_RAW(TILE, RV)                                                              \
+    do {                                                                                    \
+        const int n0_ = (TILE) * 16;                                                        \
+        QSA_LOAD_J(0, k0, v0);                                                       \
+        QSA_LOAD_J(1, k1, v1);                                                       \
+        QSA_LOAD_J(2, k2, v2);                                                       \
+        QSA_LOAD_J(3, k3, v3);                                                       \
+        QSA_LOAD_J(4, k4, v4);                                                       \
+        QSA_LOAD_J(5, k5, v5);                                                       \
+        QSA_LOAD_J(6, k6, v6);                                                       \
+        QSA_LOAD_J(7, k7, v7);                                                       \
+        /* masks of the tokens whose scores / weights this lane owns: 4 qq + i */          \
+        RV[0] = n0_ + 4 * qq + 0 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 0)] : -1;  \
+        RV[1] = n0_ + 4 * qq + 1 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 1)] : -1;  \
+        RV[2] = n0_ + 4 * qq + 2 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 2)] : -1;  \
+        RV[3] = n0_ + 4 * qq + 3 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 3)] : -1;  \
+    } while (0)
+#define QSA_STAGE_J(J, KX, VX)                                                              \
+    do {                                                                                    \
+        const int r = 2 * (J) + (lane >> 5);                                                \
+        *reinterpret_cast<uint4*>(ktile + r * kKRow + 8 * (lane & 31)) = KX;                \
+        *reinterpret_cast<uint4*>(vtile + r * kKRow + 8 * (lane & 31)) = VX;                \
+    } while (0)
+    int rv_cur[4], rv_nxt[4];
+    QSA_LOAD_RAW(wave, rv_cur);
     for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
-        const int n0 = tile * 16;
-        // slot -> row; slots past this split's end read as masked
+        // ---- stage the arrived tile (a masked row holds row 0's bytes: its weight
+        // is zeroed below and its V slice too)
+        QSA_STAGE_J(0, k0, v0);
+        QSA_STAGE_J(1, k1, v1);
+        QSA_STAGE_J(2, k2, v2);
+        QSA_STAGE_J(3, k3, v3);
+        QSA_STAGE_J(4, k4, v4);
+        QSA_STAGE_J(5, k5, v5);
+        QSA_STAGE_J(6, k6, v6);
+        QSA_STAGE_J(7, k7, v7);
+        // past the last tile every slot reads as masked: the loads then all hit
+        // row 0 (one cached line) and no branch breaks the register pipeline
+        QSA_LOAD_RAW(tile + kAttnWaves, rv_nxt);
         int rv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int nvv = n0 + 4 * qq + i;
-            rv[i] = nvv < n_s ? slot_row[slot0 + sstep * nvv] : -1;
-        }
-        // ---- issue every load of the tile.  K is read coalesced -- instruction j
-        // covers the 1 KiB of rows 2j and 2j+1 -- and staged through this wave's
-        // LDS tile, from which the MFMA layout is read back.
-        uint4 kraw[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int rl = 2 * j + (lane >> 5);  // tile row this lane loads
-            const int nr = n0 + rl;
-            const int rr = nr < n_s ? slot_row[slot0 + sstep * nr] : -1;
-            kraw[j] = *reinterpret_cast<const uint4*>(P.k + (int64_t)max(rr, 0) * kHeadDim + 8 * (lane & 31));
-        }
-        uint4 vv[4][2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint16_t* vp = P.v + (int64_t)max(rv[i], 0) * kHeadDim + 8 * c;
-            vv[i][0] = *reinterpret_cast<const uint4*>(vp);
-            vv[i][1] = *reinterpret_cast<const uint4*>(vp + 128);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<uint4*>(ktile + (2 * j + (lane >> 5)) * kKRow + 8 * (lane & 31)) = kraw[j];
+        for (int i = 0; i < 4; ++i) rv[i] = rv_cur[i];
         bf16x8 kb[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) kb[m] = *reinterpret_cast<const bf16x8*>(ktile + c * kKRow + 32 * m + 8 * qq);
+        uint4 vv[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t* vr = vtile + (4 * qq + i) * kKRow + 8 * c;
+            vv[i][0] = *reinterpret_cast<const uint4*>(vr);
+            vv[i][1] = *reinterpret_cast<const uint4*>(vr + 128);
+        }
         // ---- S^T = K . Q^T: st[i] = S[head c][token n0 + 4 qq + i]
         floatx4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -267,7 +302,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             }
             O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nt], 0, 0, 0);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rv_cur[i] = rv_nxt[i];
     }
+#undef QSA_LOAD_RAW
+#undef QSA_LOAD_J
+#undef QSA_STAGE_J
 
     // ---- merge the 4 waves in LDS
     float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -351,7 +391,7 @@ hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_i
     const int64_t nblocks = (int64_t)rows.R * kv.Hkv * num_splits;
     const int blocks_per_wg = num_splits > 1 && blocked ? (k + num_splits - 1) / num_splits : k;
     P.table_words = 4 * ((blocks_per_wg + 3) & ~3);  // keeps the K tiles 16-byte aligned
-    const size_t loop = (size_t)P.table_words * 4 + (size_t)kAttnWaves * kKTile * sizeof(uint16_t);
+    const size_t loop = (size_t)P.table_words * 4 + (size_t)kAttnWaves * 2 * kKTile * sizeof(uint16_t);
     const size_t xchg = (size_t)kAttnWaves * P.g * kHeadDim * sizeof(float);
     const size_t lds = loop > xchg ? loop : xchg;
     hipLaunchKernelGGL(attn_kernel, dim3((unsigned)nblocks), dim3(256), lds, st, P);
