@@ -56,6 +56,28 @@ def parse():
     return p.parse_args()
 
 
+LENGTH_RANGE = {"C2": "drawn uniformly from [32768, 65536]", "C5": "drawn uniformly from [65536, 131072]"}
+
+
+def describe(case) -> str:
+    """One line naming the decode workload by its shape."""
+    lo, hi = int(case.lens.min()), int(case.lens.max())
+    lens = f"length {lo}" if lo == hi else f"lengths {lo}..{hi} {LENGTH_RANGE.get(case.name, '')}".rstrip()
+    if case.block_table.shape[1] == 1:
+        cache = "contiguous bf16 KV"
+    else:
+        cache = f"bf16 paged KV ({case.page_size}-token pages{', shuffled' if case.shuffle else ''})"
+    extra = []
+    if case.jitter:
+        extra.append("per-token key/value norm jitter x U(0.5, 2)")
+    if case.bias_frac:
+        extra.append(f"{case.bias_frac:.0%} of microblocks biased +{case.bias_mag:g} sigma toward the query")
+    if case.splits > 1:
+        extra.append(f"{case.splits} split-KV partitions merged by log-sum-exp")
+    return (f"{case.name}: decode, {case.B} sequence{'s' if case.B > 1 else ''}, {lens}, ({case.Hq},{case.Hkv}) heads, "
+            f"head_dim 256, {cache}, top-{case.topk} microblocks of 4" + "".join("; " + e for e in extra))
+
+
 def source_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -277,9 +299,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic (seeded SplitMix64/Box-Muller bf16 K/V and queries)",
-        "config": {"workload": f"{case.name}: decode, {case.B} sequences, lengths U[{int(case.lens.min())}.."
-                               f"{int(case.lens.max())}] drawn from [32768, 65536], ({case.Hq},{case.Hkv}) heads, "
-                               f"head_dim 256, bf16 paged KV (64-token pages, shuffled), top-512 microblocks of 4",
+        "config": {"workload": describe(case),
                    "batch": case.B, "mean_context": float(case.lens.mean()), "topk_blocks": case.topk,
                    "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
