@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 METRIC = "QSA decode queries/s and achieved HBM GB/s (% of MI355X peak) at 64K ctx"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scores_stream_kernel_C2_traffic.json")
-SCORES_SRC = os.path.join(ROOT, "block_sparse_attention_compress_amd", "csrc", "scores.hip")
+SCORES_SRC = [os.path.join(ROOT, "block_sparse_attention_compress_amd", "csrc", f) for f in ("scores.hip", "scan_body.h")]
 
 
 def log(msg: str):
@@ -53,6 +53,7 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--graph", action="store_true", help="time a replayed HIP graph of the step instead of eager launches")
     p.add_argument("--splits", type=int, default=None, help="decode split count (default: the library's choice)")
+    p.add_argument("--no-fused", action="store_true", help="skip the single-launch fused step figures")
     return p.parse_args()
 
 
@@ -78,8 +79,11 @@ def describe(case) -> str:
             f"head_dim 256, {cache}, top-{case.topk} microblocks of 4" + "".join("; " + e for e in extra))
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def copy_calibration():
@@ -193,7 +197,8 @@ def main():
         return
     import block_sparse_attention_compress_amd as qsa
     import synth
-    from block_sparse_attention_compress_amd.pipeline import DecodeBuffers, DecodeGraph, decode_step
+    from block_sparse_attention_compress_amd.pipeline import (DecodeBuffers, DecodeGraph, FusedDecodeBuffers,
+                                                             decode_step, decode_step_fused)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     qsa.lib()
@@ -274,6 +279,24 @@ def main():
         ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
         mode = "hip-graph replay"
 
+    # (4) the fused single-launch step (qsa_decode_fused), reported beside the
+    # headline; its selection must equal the separate calls'
+    fused = None
+    if not args.no_fused:
+        fb = FusedDecodeBuffers.allocate(kv, case.Hq, case.topk, splits)
+        for _ in range(args.warmup):
+            decode_step_fused(kv, q, q_pos, fb, scale=case.scale)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            decode_step_fused(kv, q, q_pos, fb, scale=case.scale)
+        torch.cuda.synchronize()
+        fused_ms = (time.perf_counter() - t2) / args.steps * 1e3
+        fused = {"ms_per_step": round(fused_ms, 4), "queries_per_s": round(case.B / (fused_ms / 1e3), 1),
+                 "selection_equal": bool(torch.equal(fb.sel_idx, buf.sel_idx)),
+                 "abandoned_waits": int(fb.workspace[8:12].view(torch.int32).item())}
+        del fb
+
     sel = buf.sel_idx.cpu().numpy()
     cnt = buf.sel_cnt.cpu().numpy()
     step_bytes, scores_bytes, tokens = decode_bytes(case, sel, cnt, case.page_size)
@@ -310,7 +333,7 @@ def main():
                  "selected_tokens": tokens,
                  "event_ms": {"compress_refresh": round(part_ms[0], 5), "block_scores": round(part_ms[1], 5),
                               "topk": round(part_ms[2], 5), "attention_and_merge": round(part_ms[3], 5)},
-                 "execution": mode, "eager_ms_per_step": round(eager_ms, 4),
+                 "execution": mode, "eager_ms_per_step": round(eager_ms, 4), "fused_single_launch": fused,
                  "full_block_key_build_ms": round(compress_full_ms, 4)},
     }
     if not args.no_extend:

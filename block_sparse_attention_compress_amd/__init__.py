@@ -7,7 +7,8 @@ declarations, with the meaning, layout and error behaviour of every argument,
 are in ``include/qsa.h``.  The functions keep the C names:
 
     qsa_compress_keys, qsa_block_scores, qsa_topk_blocks,
-    qsa_sparse_attn_decode, qsa_sparse_attn_extend, qsa_merge_lse
+    qsa_sparse_attn_decode, qsa_sparse_attn_extend, qsa_merge_lse,
+    qsa_decode_fused (scores + top-k + attention + merge in one launch)
 
 Importing this module does not need a GPU; calling a function that launches
 work does.  If ``libqsa.so`` has not been built, loading fails with an error:
@@ -34,7 +35,8 @@ MAX_TOPK = 2048
 MAX_SPLITS = 64
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks",
-           "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse")
+           "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse",
+           "qsa_decode_fused", "qsa_decode_fused_workspace_bytes")
 
 
 class QsaError(RuntimeError):
@@ -82,8 +84,11 @@ def lib() -> ctypes.CDLL:
         L.qsa_decode_workspace_bytes.argtypes, L.qsa_decode_workspace_bytes.restype = [i32, i32, i32], sz
         L.qsa_sparse_attn_extend.argtypes = [kvp, vp, i64, vp, vp, i32, i32, vp, vp, i32, f32, vp, i64, vp, vp]
         L.qsa_merge_lse.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+        L.qsa_decode_fused.argtypes = [kvp, vp, i64, i32, i32, f32, i32, vp, vp, vp, i64, vp, vp, sz, vp]
+        L.qsa_decode_fused_workspace_bytes.argtypes = [kvp, i32, i32, i32]
+        L.qsa_decode_fused_workspace_bytes.restype = sz
         for f in ("qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks", "qsa_sparse_attn_decode",
-                  "qsa_sparse_attn_extend", "qsa_merge_lse"):
+                  "qsa_sparse_attn_extend", "qsa_merge_lse", "qsa_decode_fused"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,3 +190,17 @@ def qsa_sparse_attn_extend(kv, q, q_row_stride: int, q_seq, q_pos, R: int, Hq: i
 
 def qsa_merge_lse(part_out, part_lse, S: int, N: int, D: int, out, out_lse=None, stream=None) -> None:
     _check(lib().qsa_merge_lse(_ptr(part_out), _ptr(part_lse), S, N, D, _ptr(out), _ptr(out_lse), _stream(stream)))
+
+
+def qsa_decode_fused_workspace_bytes(kv, Hq: int, k: int, num_splits: int = 0) -> int:
+    d = _kv(kv)
+    return int(lib().qsa_decode_fused_workspace_bytes(ctypes.byref(d), Hq, k, num_splits))
+
+
+def qsa_decode_fused(kv, q, q_row_stride: int, Hq: int, k: int, scale: float, num_splits: int, sel_idx, sel_cnt,
+                     out, out_row_stride: int, lse=None, workspace=None, workspace_bytes: int = 0,
+                     stream=None) -> None:
+    d = _kv(kv)
+    _check(lib().qsa_decode_fused(ctypes.byref(d), _ptr(q), q_row_stride, Hq, k, scale, num_splits, _ptr(sel_idx),
+                                  _ptr(sel_cnt), _ptr(out), out_row_stride, _ptr(lse), _ptr(workspace),
+                                  workspace_bytes, _stream(stream)))

@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libqsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["qsa_api.hip", "compress.hip", "scores.hip", "topk.hip", "attn.hip", "merge.hip"]
+SOURCES = ["qsa_api.hip", "compress.hip", "scores.hip", "topk.hip", "attn.hip", "merge.hip", "fused.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950",

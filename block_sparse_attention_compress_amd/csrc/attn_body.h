@@ -1,0 +1,331 @@
+// Exact softmax attention of one (row, KV head, split) work unit over the tokens
+// of its selected blocks.  Used by attn_kernel (decode and extend) and by the
+// fused decode kernel.  The design (matrix-core tiles, lazy-rescaled online
+// softmax, LDS staging) is described at the top of attn.hip.
+#pragma once
+
+#include "qsa_device.h"
+
+namespace qsa {
+
+constexpr int kAttnWaves = 4;
+constexpr int kMaxSel = 2048;
+constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
+constexpr int kKRow = kHeadDim + 8;   // padded K row in the LDS tile (elements): spreads rows over banks
+constexpr int kKTile = 16 * kKRow;    // one wave's K (or V) tile (elements)
+
+typedef short bf16x4s __attribute__((ext_vector_type(4)));
+
+struct AttnParams {
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int Hkv, lg_ps, max_pages;
+    const uint16_t* q;
+    int64_t q_stride;
+    const int32_t* q_seq;
+    const int32_t* q_pos;
+    int R, Hq, g;
+    const int32_t* sel;
+    const int32_t* cnt;
+    int kstride;
+    float scale_log2;
+    int S;
+    int blocked;  // 1: split s takes a contiguous range of selected blocks; 0: token slots p mod S
+    int table_words;  // int32 words of LDS reserved for the slot table
+    uint16_t* out;
+    int64_t out_stride;
+    float* lse;
+    float* part_out;
+    float* part_lse;
+};
+
+__device__ __forceinline__ uint32_t u4_word(const uint4& a, int w) {
+    return w == 0 ? a.x : (w == 1 ? a.y : (w == 2 ? a.z : a.w));
+}
+
+// LDS: `smem` is dynamic shared memory of the launch: the slot table (16 B per
+// selected block of this work unit, P.table_words int32) and the 4 waves' K and V
+// staging tiles, later reused for the waves' O exchange (4 waves x g heads x
+// 1 KiB); the launch sizes it to the larger need.  Ends with a barrier-free
+// write of the result; the caller separates work units sharing `smem` with a
+// barrier.
+__device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h, int s, float* smem) {
+    __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
+    int32_t* slot_row = reinterpret_cast<int32_t*>(smem);
+    const int S = P.S;
+    const int seq = P.q_seq ? P.q_seq[row] : row;
+    const int L = P.seq_lens[seq];
+    const int t = P.q_pos ? P.q_pos[row] : L - 1;
+    const int64_t lim = min((int64_t)L, (int64_t)t + 1);  // tokens at positions < lim are visible
+    const int g = P.g;
+    const int tid = threadIdx.x;
+
+    const int lane = tid & 63;
+    const int wave = wave_id();
+    const int c = lane & 15;
+    const int qq = lane >> 4;
+
+    // The query, the count and the selection are independent reads: issue them
+    // together.  Blocked splits cut the k selection slots (not the count), so the
+    // selection reads need not wait for the count.
+    bf16x8 qb[8];
+    {
+        const uint16_t* qp = P.q + (int64_t)row * P.q_stride + (int64_t)(h * g + min(c, g - 1)) * kHeadDim + 8 * qq;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 32 * m);
+        if (c >= g) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) qb[m] = bf16x8{};
+        }
+    }
+    const int cnt_raw = P.cnt[(int64_t)row * P.Hkv + h];
+    int jb = 0, jcap = P.kstride;
+    if (P.blocked) {
+        const int per = (P.kstride + S - 1) / S;
+        jb = min(P.kstride, s * per);
+        jcap = min(P.kstride, jb + per);
+    }
+    const int32_t* sel_row = P.sel + ((int64_t)row * P.Hkv + h) * P.kstride;
+    constexpr int kIt = kMaxSel / 256;
+    int bsel[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int j = jb + tid + 256 * it;
+        bsel[it] = j < jcap ? sel_row[j] : -1;
+    }
+    // selected blocks [jb, je) feed this workgroup; the table holds their slots
+    const int nsel = max(0, min(cnt_raw, P.kstride));
+    const int je = max(jb, min(nsel, jcap));
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int j = jb + tid + 256 * it;
+        if (j >= je) break;
+        const int b = bsel[it];
+        const int64_t pos0 = 4 * (int64_t)b;
+        int32_t base = 0;
+        int nv = 0;
+        if (b >= 0 && pos0 < lim) {
+            base = (int32_t)token_row(P.block_table, seq, P.max_pages, P.Hkv, h, P.lg_ps, pos0);
+            nv = (int)min(lim - pos0, (int64_t)4);
+        }
+        *reinterpret_cast<int4*>(slot_row + 4 * (j - jb)) = make_int4(
+            nv > 0 ? base : -1, nv > 1 ? base + 1 : -1, nv > 2 ? base + 2 : -1, nv > 3 ? base + 3 : -1);
+    }
+    __syncthreads();
+
+    // split-local slot n lives at table entry slot0 + sstep * n
+    const int ntok = 4 * (je - jb);
+    int n_s, slot0, sstep;
+    if (P.blocked) {
+        n_s = ntok;
+        slot0 = 0;
+        sstep = 1;
+    } else {
+        n_s = ntok > s ? (ntok - s + S - 1) / S : 0;
+        slot0 = s;
+        sstep = S;
+    }
+    const int ntiles = (n_s + 15) / 16;
+    uint16_t* ktile = reinterpret_cast<uint16_t*>(smem + P.table_words) + wave * 2 * kKTile;
+    uint16_t* vtile = ktile + kKTile;
+
+    float m_run = -INFINITY;  // reference max of head c (log2 units), same in every qq group
+    float l_run = 0.f;        // this lane's share of the head's normaliser
+    floatx4 O[16];
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Raw tile loads are coalesced -- instruction j covers the 1 KiB of tile rows
+    // 2j and 2j+1 -- and land in this wave's LDS tiles, from which the MFMA
+    // layouts are read.  The loads of tile i+1 are issued before tile i is
+    // computed, so a wave always has a tile in flight.
+    // (the raw tile is 16 named registers, not an array: an array indexed in a
+    // loop across the tile pipeline was kept in scratch memory)
+    uint4 k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+#define QSA_LOAD_J(J, KX, VX)                                                               \
+    do {                                                                                    \
+        const int nr = n0_ + 2 * (J) + (lane >> 5);                                         \
+        const int rr = nr < n_s ? slot_row[slot0 + sstep * nr] : -1;                        \
+        const int64_t off = (int64_t)max(rr, 0) * kHeadDim + 8 * (lane & 31);               \
+        KX = *reinterpret_cast<const uint4*>(P.k + off);                                    \
+        VX = *reinterpret_cast<const uint4*>(P.v + off);                                    \
+    } while (0)
+#define QSA_LOAD_RAW(TILE, RV)                                                              \
+    do {                                                                                    \
+        const int n0_ = (TILE) * 16;                                                        \
+        QSA_LOAD_J(0, k0, v0);                                                       \
+        QSA_LOAD_J(1, k1, v1);                                                       \
+        QSA_LOAD_J(2, k2, v2);                                                       \
+        QSA_LOAD_J(3, k3, v3);                                                       \
+        QSA_LOAD_J(4, k4, v4);                                                       \
+        QSA_LOAD_J(5, k5, v5);                                                       \
+        QSA_LOAD_J(6, k6, v6);                                                       \
+        QSA_LOAD_J(7, k7, v7);                                                       \
+        /* masks of the tokens whose scores / weights this lane owns: 4 qq + i */          \
+        RV[0] = n0_ + 4 * qq + 0 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 0)] : -1;  \
+        RV[1] = n0_ + 4 * qq + 1 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 1)] : -1;  \
+        RV[2] = n0_ + 4 * qq + 2 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 2)] : -1;  \
+        RV[3] = n0_ + 4 * qq + 3 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 3)] : -1;  \
+    } while (0)
+#define QSA_STAGE_J(J, KX, VX)                                                              \
+    do {                                                                                    \
+        const int r = 2 * (J) + (lane >> 5);                                                \
+        *reinterpret_cast<uint4*>(ktile + r * kKRow + 8 * (lane & 31)) = KX;                \
+        *reinterpret_cast<uint4*>(vtile + r * kKRow + 8 * (lane & 31)) = VX;                \
+    } while (0)
+    int rv_cur[4], rv_nxt[4];
+    QSA_LOAD_RAW(wave, rv_cur);
+    for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
+        // ---- stage the arrived tile (a masked row holds row 0's bytes: its weight
+        // is zeroed below and its V slice too)
+        QSA_STAGE_J(0, k0, v0);
+        QSA_STAGE_J(1, k1, v1);
+        QSA_STAGE_J(2, k2, v2);
+        QSA_STAGE_J(3, k3, v3);
+        QSA_STAGE_J(4, k4, v4);
+        QSA_STAGE_J(5, k5, v5);
+        QSA_STAGE_J(6, k6, v6);
+        QSA_STAGE_J(7, k7, v7);
+        // past the last tile every slot reads as masked: the loads then all hit
+        // row 0 (one cached line) and no branch breaks the register pipeline
+        QSA_LOAD_RAW(tile + kAttnWaves, rv_nxt);
+        int rv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rv[i] = rv_cur[i];
+        bf16x8 kb[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) kb[m] = *reinterpret_cast<const bf16x8*>(ktile + c * kKRow + 32 * m + 8 * qq);
+        uint4 vv[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t* vr = vtile + (4 * qq + i) * kKRow + 8 * c;
+            vv[i][0] = *reinterpret_cast<const uint4*>(vr);
+            vv[i][1] = *reinterpret_cast<const uint4*>(vr + 128);
+        }
+        // ---- S^T = K . Q^T: st[i] = S[head c][token n0 + 4 qq + i]
+        floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[m], qb[m], st, 0, 0, 0);
+        float x[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = rv[i] >= 0 ? st[i] * P.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, x[i]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // ---- lazy rescale: only when some head's max passes its reference by 2^8
+        if (__ballot(mx > m_run + kLazy)) {
+            const float m_new = mx > m_run + kLazy ? fmaxf(m_run, mx) : m_run;
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a_i = __shfl(alpha, 4 * qq + i);
+#pragma unroll
+                for (int nt = 0; nt < 16; ++nt) O[nt][i] *= a_i;
+            }
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        uint32_t pw[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const uint32_t lo = f32_to_bf16_rne(__builtin_amdgcn_exp2f(x[2 * w] - m_use));
+            const uint32_t hi = f32_to_bf16_rne(__builtin_amdgcn_exp2f(x[2 * w + 1] - m_use));
+            psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
+            pw[w] = lo | (hi << 16);
+        }
+        l_run += psum;
+        // ---- zero the V of masked slots (their weight is 0, their bytes may be anything)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (rv[i] < 0) {
+                vv[i][0] = make_uint4(0, 0, 0, 0);
+                vv[i][1] = make_uint4(0, 0, 0, 0);
+            }
+        // ---- O += P . V; k-slot i of lane (., qq) is token n0 + 4 qq + i
+        bf16x4s pa;
+        {
+            uint32_t* p32 = reinterpret_cast<uint32_t*>(&pa);
+            p32[0] = pw[0];
+            p32[1] = pw[1];
+        }
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt) {
+            const int hf = nt >> 3, e = (nt & 7) >> 1;  // dim 128 hf + 8c + (nt & 7): dword e of half hf
+            const uint32_t d0 = u4_word(vv[0][hf], e), d1 = u4_word(vv[1][hf], e);
+            const uint32_t d2 = u4_word(vv[2][hf], e), d3 = u4_word(vv[3][hf], e);
+            bf16x4s vb;
+            uint32_t* v32 = reinterpret_cast<uint32_t*>(&vb);
+            if (nt & 1) {
+                v32[0] = (d0 >> 16) | (d1 & 0xffff0000u);
+                v32[1] = (d2 >> 16) | (d3 & 0xffff0000u);
+            } else {
+                v32[0] = (d0 & 0xffffu) | (d1 << 16);
+                v32[1] = (d2 & 0xffffu) | (d3 << 16);
+            }
+            O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rv_cur[i] = rv_nxt[i];
+    }
+#undef QSA_LOAD_RAW
+#undef QSA_LOAD_J
+#undef QSA_STAGE_J
+
+    // ---- merge the 4 waves in LDS
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    __syncthreads();  // the slot table is dead; smem becomes the O exchange
+    if (qq == 0) {
+        wm[wave][c] = m_run;
+        wl[wave][c] = l_tot;
+    }
+    float* ow = smem + wave * g * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * qq + i < g) {
+#pragma unroll
+            for (int nt = 0; nt < 16; ++nt)
+                ow[(4 * qq + i) * kHeadDim + 128 * (nt >> 3) + 8 * c + (nt & 7)] = O[nt][i];
+        }
+    __syncthreads();
+
+    const float kLn2 = 0.6931471805599453f;
+    for (int e = tid; e < g * kHeadDim; e += 256) {
+        const int hh = e >> 8;
+        const int d = e & (kHeadDim - 1);
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wl[w][hh] > 0.f ? wm[w][hh] : -INFINITY);
+        float o = 0.f, lse_v = -INFINITY;
+        if (M != -INFINITY) {
+            float num = 0.f, den = 0.f;
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) {
+                if (!(wl[w][hh] > 0.f)) continue;
+                const float f = __builtin_amdgcn_exp2f(wm[w][hh] - M);
+                num += f * smem[(w * g + hh) * kHeadDim + d];
+                den += f * wl[w][hh];
+            }
+            o = num / den;
+            lse_v = (M + __log2f(den)) * kLn2;
+        }
+        const int head = h * g + hh;
+        if (P.part_out) {
+            const int64_t prow = ((int64_t)s * P.R + row) * P.Hq + head;
+            P.part_out[prow * kHeadDim + d] = o;
+            if (d == 0) P.part_lse[prow] = lse_v;
+        } else {
+            P.out[(int64_t)row * P.out_stride + (int64_t)head * kHeadDim + d] = (uint16_t)f32_to_bf16_rne(o);
+            if (d == 0 && P.lse) P.lse[(int64_t)row * P.Hq + head] = lse_v;
+        }
+    }
+}
+
+}  // namespace qsa

@@ -224,6 +224,44 @@ int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
                       "qsa_sparse_attn_decode (merge)");
 }
 
+size_t qsa_decode_fused_workspace_bytes(const qsa_kv_t* kv, int32_t Hq, int32_t k, int32_t num_splits) {
+    if (!kv || kv->batch < 0 || kv->num_kv_heads < 1 || Hq < 1 || kv->max_seq_len < 0 ||
+        kv->max_seq_len > QSA_MAX_SEQ_LEN || k < 0 || k > QSA_MAX_TOPK || num_splits < 0 ||
+        num_splits > QSA_MAX_SPLITS)
+        return 0;
+    const int S = num_splits == 0 ? auto_splits((int64_t)kv->batch * kv->num_kv_heads, k) : num_splits;
+    return qsa::fused_workspace_bytes(kv->batch, kv->num_kv_heads, Hq, kv->max_seq_len, S);
+}
+
+int qsa_decode_fused(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq, int32_t k, float scale,
+                     int32_t num_splits, int32_t* sel_idx, int32_t* sel_cnt, void* out, int64_t out_row_stride,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, true, true, true, &p)) return rc;
+    if (int rc = check_heads(Hq, p.Hkv)) return rc;
+    if (int rc = check_q(q, q_row_stride, Hq)) return rc;
+    if (k < 0 || k > QSA_MAX_TOPK) return fail(QSA_ERR_INVALID_ARG, "k %d out of [0, %d]", k, QSA_MAX_TOPK);
+    if (!sel_cnt || (k > 0 && !sel_idx)) return fail(QSA_ERR_INVALID_ARG, "sel_idx / sel_cnt is NULL");
+    if (num_splits < 0 || num_splits > QSA_MAX_SPLITS)
+        return fail(QSA_ERR_INVALID_ARG, "num_splits %d out of [0, %d]", num_splits, QSA_MAX_SPLITS);
+    if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned(out, 8) || out_row_stride < (int64_t)Hq * QSA_HEAD_DIM || out_row_stride % 4)
+        return fail(QSA_ERR_INVALID_ARG, "out must be 8-byte aligned with a row stride >= Hq * 256, a multiple of 4");
+    const int S = num_splits == 0 ? auto_splits((int64_t)p.batch * p.Hkv, k) : num_splits;
+    const int64_t units = (int64_t)p.batch * p.Hkv;
+    const int64_t chunks = ((int64_t)p.max_seq_len + 3) / 4 / 128 + 2;
+    if (units * (chunks + S) > 0x7fffffff) return fail(QSA_ERR_UNSUPPORTED, "too many work items");
+    const size_t need = qsa::fused_workspace_bytes(p.batch, p.Hkv, Hq, p.max_seq_len, S);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(QSA_ERR_INVALID_ARG, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    const float sc = scale > 0.f ? scale : 0.0625f;
+    qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, nullptr, nullptr, p.batch, Hq};
+    return hip_status(qsa::launch_fused_decode(p, rows, k, sc, S, sel_idx, sel_cnt, static_cast<uint16_t*>(out),
+                                               out_row_stride, lse, workspace, static_cast<hipStream_t>(stream)),
+                      "qsa_decode_fused");
+}
+
 int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
                            const int32_t* q_pos, int32_t R, int32_t Hq, const int32_t* sel_idx,
                            const int32_t* sel_cnt, int32_t k, float scale, void* out, int64_t out_row_stride,

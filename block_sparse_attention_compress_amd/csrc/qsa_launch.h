@@ -50,6 +50,15 @@ struct AttnOut {
 hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt, int k,
                        float scale, int num_splits, bool blocked, const AttnOut& o, hipStream_t st);
 
+// Fused decode (scores, top-k, attention, merge in one persistent launch) with S
+// attention splits per (row, KV head); workspace laid out by fused_workspace_bytes,
+// its first fused_control_bytes zero before the call and zero after it.
+size_t fused_workspace_bytes(int batch, int Hkv, int Hq, int max_seq_len, int S);
+size_t fused_control_bytes(int batch, int Hkv);
+hipError_t launch_fused_decode(const PagedKV& kv, const Rows& rows, int k, float scale, int S, int32_t* sel_idx,
+                               int32_t* sel_cnt, uint16_t* out, int64_t out_stride, float* lse, void* workspace,
+                               hipStream_t st);
+
 hipError_t launch_merge(const float* part_out, const float* part_lse, int S, int N, int D, uint16_t* out,
                         float* out_lse, hipStream_t st);
 

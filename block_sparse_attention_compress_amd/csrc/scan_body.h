@@ -1,0 +1,125 @@
+// One wave's share of the decode block-score scan: 16 blocks at a time, each
+// lane one float4 of each block key, 16 dot products folded by a reduce-scatter
+// butterfly.  Used by scores_stream_kernel and by the fused decode kernel.
+#pragma once
+
+#include "qsa_device.h"
+
+namespace qsa {
+
+// blocks per workgroup: 4 waves x 2 groups of 16.  Smaller chunks spread the
+// rows over more workgroups (32 rows of 32K-64K tokens, 16 heads: 256 -> 128
+// took the scan from 152 to 144 us; 64 was no faster).
+constexpr int kStreamChunk = 128;
+constexpr int kGroups = kStreamChunk / 64;  // 16-block groups per wave
+
+// Scores of blocks [wb0, wb0 + 16 kGroups) ∩ [0, n_elig) of one (row, KV head):
+//   srow[b] = (sum of the g query heads at qrow) . ckey[b]
+// qrow: the row's first query head of the group (bf16 [g][256]); bt: the
+// sequence's block-table row.  Requires wb0 < n_elig.
+// PAGE16: a page holds >= 16 blocks (page_size >= 64).  A wave's group of 16
+// blocks starts 16-aligned, so it lies in one page: one block-table lookup gives
+// 16 KiB of contiguous block keys, and the loads need no per-block branch (slots
+// past the row end are still inside the page; their sums are never written).
+// COHERENT: scores are stored at device scope (written through to where every
+// CU reads them), for a reader in another workgroup of the same launch.
+template <bool PAGE16, bool COHERENT = false>
+__device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int g, const float* __restrict__ ckey,
+                                          const int32_t* __restrict__ bt, int Hkv, int h, int lg_ps, int n_elig,
+                                          int wb0, int lane, float* __restrict__ srow) {
+    const int lg_bpp = lg_ps - 2;  // blocks per page = page_size / 4
+    // block-key rows of the wave's groups (PAGE16), looked up before any wait
+    int64_t gbase[kGroups];
+    if (PAGE16) {
+#pragma unroll
+        for (int grp = 0; grp < kGroups; ++grp) {
+            const int b0 = min(wb0 + grp * 16, n_elig - 1) & ~15;
+            gbase[grp] = (((int64_t)bt[b0 >> lg_bpp] * Hkv + h) << lg_bpp) + (b0 & ((1 << lg_bpp) - 1));
+        }
+    }
+
+    auto load_group = [&](int grp, float4* v) {
+        const int b0 = wb0 + grp * 16;
+        if (PAGE16) {
+            const float* src = ckey + gbase[grp] * kHeadDim + 4 * lane;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = *reinterpret_cast<const float4*>(src + j * kHeadDim);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int b = min(b0 + j, n_elig - 1);
+                const int64_t page = bt[b >> lg_bpp];
+                const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
+                v[j] = *reinterpret_cast<const float4*>(ckey + brow * kHeadDim + 4 * lane);
+            }
+        }
+    };
+    // the first group's block keys are requested before the query
+    float4 v[16];
+    load_group(0, v);
+
+    // group-summed query: lane holds dims 4*lane .. 4*lane+3; the g loads are
+    // issued together (one wait), summed in head order
+    float4 qs = make_float4(0.f, 0.f, 0.f, 0.f);
+    {
+        const uint16_t* qp = qrow + 4 * lane;
+        uint2 qw[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qw[j] = j < g ? *reinterpret_cast<const uint2*>(qp + j * kHeadDim) : make_uint2(0, 0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            qs.x += bf16_lo(qw[j].x);
+            qs.y += bf16_hi(qw[j].x);
+            qs.z += bf16_lo(qw[j].y);
+            qs.w += bf16_hi(qw[j].y);
+        }
+    }
+
+    for (int grp = 0; grp < kGroups; ++grp) {
+        const int b0 = wb0 + grp * 16;
+        if (b0 >= n_elig) break;
+        float p[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = qs.x * v[j].x + qs.y * v[j].y + qs.z * v[j].z + qs.w * v[j].w;
+        // the next group's loads fly while this group is reduced
+        if (grp < kGroups - 1 && b0 + 16 < n_elig) load_group(grp + 1, v);
+        // reduce-scatter: after the step across lane bit m (m = 5, 4, 3, 2) a lane
+        // keeps the half of its blocks selected by that bit; finally lane l holds
+        // the full sum of block l >> 2 (lanes differing in bits 0, 1 agree).  Each
+        // block's partial sums only ever meet each other.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool up = lane & 32;
+            const float keep = up ? p[i + 8] : p[i], send = up ? p[i] : p[i + 8];
+            p[i] = keep + __shfl_xor(send, 32);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool up = lane & 16;
+            const float keep = up ? p[i + 4] : p[i], send = up ? p[i] : p[i + 4];
+            p[i] = keep + __shfl_xor(send, 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bool up = lane & 8;
+            const float keep = up ? p[i + 2] : p[i], send = up ? p[i] : p[i + 2];
+            p[i] = keep + __shfl_xor(send, 8);
+        }
+        {
+            const bool up = lane & 4;
+            const float keep = up ? p[1] : p[0], send = up ? p[0] : p[1];
+            p[0] = keep + __shfl_xor(send, 4);
+        }
+        p[0] += __shfl_xor(p[0], 2);
+        p[0] += __shfl_xor(p[0], 1);
+        const int b = b0 + (lane >> 2);
+        if ((lane & 3) == 0 && b < n_elig) {
+            if (COHERENT)
+                __hip_atomic_store(srow + b, p[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                srow[b] = p[0];
+        }
+    }
+}
+
+}  // namespace qsa

@@ -18,19 +18,10 @@
 //    matrix-core tiles, 16 rows per wave.
 #include "qsa_device.h"
 #include "qsa_launch.h"
+#include "scan_body.h"
 
 namespace qsa {
 
-// blocks per workgroup: 4 waves x 2 groups of 16.  Smaller chunks spread the
-// rows over more workgroups (32 rows of 32K-64K tokens, 16 heads: 256 -> 128
-// took the scan from 152 to 144 us; 64 was no faster).
-constexpr int kStreamChunk = 128;
-constexpr int kGroups = kStreamChunk / 64;  // 16-block groups per wave
-
-// PAGE16: a page holds >= 16 blocks (page_size >= 64).  A wave's group of 16
-// blocks starts 16-aligned, so it lies in one page: one block-table lookup gives
-// 16 KiB of contiguous block keys, and the loads need no per-block branch (slots
-// past the row end are still inside the page; their sums are never written).
 template <bool PAGE16>
 __global__ __launch_bounds__(256) void scores_stream_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
@@ -50,97 +41,9 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
     const int wave = wave_id();
     const int wb0 = chunk0 + wave * (kStreamChunk / 4);  // this wave's first block
     if (wb0 >= n_elig) return;
-
-    const int lg_bpp = lg_ps - 2;  // blocks per page = page_size / 4
-    const int32_t* bt = block_table + (int64_t)seq * max_pages;
-    // block-key rows of the wave's groups (PAGE16), looked up before any wait
-    int64_t gbase[kGroups];
-    if (PAGE16) {
-#pragma unroll
-        for (int grp = 0; grp < kGroups; ++grp) {
-            const int b0 = min(wb0 + grp * 16, n_elig - 1) & ~15;
-            gbase[grp] = (((int64_t)bt[b0 >> lg_bpp] * Hkv + h) << lg_bpp) + (b0 & ((1 << lg_bpp) - 1));
-        }
-    }
-
-    auto load_group = [&](int grp, float4* v) {
-        const int b0 = wb0 + grp * 16;
-        if (PAGE16) {
-            const float* src = ckey + gbase[grp] * kHeadDim + 4 * lane;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = *reinterpret_cast<const float4*>(src + j * kHeadDim);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int b = min(b0 + j, n_elig - 1);
-                const int64_t page = bt[b >> lg_bpp];
-                const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
-                v[j] = *reinterpret_cast<const float4*>(ckey + brow * kHeadDim + 4 * lane);
-            }
-        }
-    };
-    // the first group's block keys are requested before the query
-    float4 v[16];
-    load_group(0, v);
-
-    // group-summed query: lane holds dims 4*lane .. 4*lane+3; the g loads are
-    // issued together (one wait), summed in head order
-    float4 qs = make_float4(0.f, 0.f, 0.f, 0.f);
-    {
-        const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + 4 * lane;
-        uint2 qw[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) qw[j] = j < g ? *reinterpret_cast<const uint2*>(qrow + j * kHeadDim) : make_uint2(0, 0);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            qs.x += bf16_lo(qw[j].x);
-            qs.y += bf16_hi(qw[j].x);
-            qs.z += bf16_lo(qw[j].y);
-            qs.w += bf16_hi(qw[j].y);
-        }
-    }
-
-    float* srow = scores + ((int64_t)row * Hkv + h) * score_stride;
-    for (int grp = 0; grp < kGroups; ++grp) {
-        const int b0 = wb0 + grp * 16;
-        if (b0 >= n_elig) break;
-        float p[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] = qs.x * v[j].x + qs.y * v[j].y + qs.z * v[j].z + qs.w * v[j].w;
-        // the next group's loads fly while this group is reduced
-        if (grp < kGroups - 1 && b0 + 16 < n_elig) load_group(grp + 1, v);
-        // reduce-scatter: after the step across lane bit m (m = 5, 4, 3, 2) a lane
-        // keeps the half of its blocks selected by that bit; finally lane l holds
-        // the full sum of block l >> 2 (lanes differing in bits 0, 1 agree).  Each
-        // block's partial sums only ever meet each other.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bool up = lane & 32;
-            const float keep = up ? p[i + 8] : p[i], send = up ? p[i] : p[i + 8];
-            p[i] = keep + __shfl_xor(send, 32);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool up = lane & 16;
-            const float keep = up ? p[i + 4] : p[i], send = up ? p[i] : p[i + 4];
-            p[i] = keep + __shfl_xor(send, 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const bool up = lane & 8;
-            const float keep = up ? p[i + 2] : p[i], send = up ? p[i] : p[i + 2];
-            p[i] = keep + __shfl_xor(send, 8);
-        }
-        {
-            const bool up = lane & 4;
-            const float keep = up ? p[1] : p[0], send = up ? p[0] : p[1];
-            p[0] = keep + __shfl_xor(send, 4);
-        }
-        p[0] += __shfl_xor(p[0], 2);
-        p[0] += __shfl_xor(p[0], 1);
-        const int b = b0 + (lane >> 2);
-        if ((lane & 3) == 0 && b < n_elig) srow[b] = p[0];
-    }
+    scan_wave<PAGE16>(q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim, g, ckey,
+                      block_table + (int64_t)seq * max_pages, Hkv, h, lg_ps, n_elig, wb0, lane,
+                      scores + ((int64_t)row * Hkv + h) * score_stride);
 }
 
 // Extend: 64 rows per workgroup, 16 per wave.  Lane (c = lane & 15, kq = lane >> 4)

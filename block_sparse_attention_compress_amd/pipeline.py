@@ -11,8 +11,9 @@ from typing import Optional
 
 import torch
 
-from . import (HEAD_DIM, KVCache, qsa_block_scores, qsa_compress_keys, qsa_decode_workspace_bytes,
-               qsa_sparse_attn_decode, qsa_sparse_attn_extend, qsa_topk_blocks)
+from . import (HEAD_DIM, KVCache, qsa_block_scores, qsa_compress_keys, qsa_decode_fused,
+               qsa_decode_fused_workspace_bytes, qsa_decode_workspace_bytes, qsa_sparse_attn_decode,
+               qsa_sparse_attn_extend, qsa_topk_blocks)
 
 
 @dataclass
@@ -57,6 +58,45 @@ def decode_step(kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: DecodeBu
     qsa_sparse_attn_decode(kv, q, q.stride(0), Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale, num_splits, buf.out,
                            buf.out.stride(0), buf.lse, workspace=ws, workspace_bytes=0 if ws is None else ws.numel(),
                            stream=stream)
+
+
+@dataclass
+class FusedDecodeBuffers:
+    """Outputs and workspace of the fused decode step.  The workspace is zeroed
+    once here; the library leaves its control area zero after every call."""
+
+    sel_idx: torch.Tensor     # int32 [B][Hkv][k]
+    sel_cnt: torch.Tensor     # int32 [B][Hkv]
+    out: torch.Tensor         # bf16 [B][Hq][256]
+    lse: torch.Tensor         # fp32 [B][Hq]
+    workspace: torch.Tensor   # uint8, zero-filled at allocation
+    k: int
+    num_splits: int
+
+    @staticmethod
+    def allocate(kv: KVCache, Hq: int, k: int, num_splits: int = 0, device="cuda") -> "FusedDecodeBuffers":
+        B, Hkv = kv.block_table.shape[0], kv.k.shape[1]
+        ws = qsa_decode_fused_workspace_bytes(kv, Hq, k, num_splits)
+        if ws == 0:
+            raise ValueError("invalid fused decode shape")
+        return FusedDecodeBuffers(
+            sel_idx=torch.empty((B, Hkv, max(k, 1)), dtype=torch.int32, device=device),
+            sel_cnt=torch.empty((B, Hkv), dtype=torch.int32, device=device),
+            out=torch.empty((B, Hq, HEAD_DIM), dtype=torch.bfloat16, device=device),
+            lse=torch.empty((B, Hq), dtype=torch.float32, device=device),
+            workspace=torch.zeros(ws, dtype=torch.uint8, device=device), k=k, num_splits=num_splits)
+
+
+def decode_step_fused(kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: FusedDecodeBuffers, scale: float = 0.0,
+                      refresh_keys: bool = True, stream=None) -> None:
+    """The decode step in two launches: the block-key refresh of the newest token,
+    then scores, selection, attention and merge fused."""
+    Hq = q.shape[1]
+    if refresh_keys:
+        qsa_compress_keys(kv, q_pos, 1, stream=stream)
+    qsa_decode_fused(kv, q, q.stride(0), Hq, buf.k, scale, buf.num_splits, buf.sel_idx, buf.sel_cnt, buf.out,
+                     buf.out.stride(0), buf.lse, workspace=buf.workspace, workspace_bytes=buf.workspace.numel(),
+                     stream=stream)
 
 
 @dataclass

@@ -170,6 +170,36 @@ QSA_API int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_
 QSA_API size_t qsa_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t num_splits);
 
 /*
+ * Fused decode: a2 + a3 + a4 + a5 of one decode step in a single launch -- the
+ * same block scores, the same top-k order and selection, and the same split
+ * attention and log-sum-exp merge as the separate calls above, with the steps
+ * of different (sequence, KV head) units overlapping.  Block keys must be
+ * current (qsa_compress_keys first, as for qsa_block_scores).
+ *   sel_idx int32 [batch][Hkv][k] and sel_cnt int32 [batch][Hkv] receive the
+ *     selection, exactly as qsa_topk_blocks writes it;
+ *   out bf16 at out + row * out_row_stride ([Hq][256] per row, 8-byte aligned,
+ *     stride a multiple of 4) and lse fp32 [batch][Hq] (may be NULL) receive
+ *     the result, as qsa_sparse_attn_decode writes it;
+ *   num_splits: attention splits per (sequence, KV head), 0 = the library's
+ *     choice; the result does not depend on it beyond rounding.
+ * workspace: qsa_decode_fused_workspace_bytes(kv, Hq, k, num_splits) bytes,
+ * 256-byte aligned.  It holds the scores, the partials and a control area of
+ * counters and flags that must be all zero when the call starts: zero-fill the
+ * workspace once before its first use; every call leaves the control area zero
+ * again, so later calls need no clearing.  Calls that share a workspace must
+ * not overlap (issue them on one stream).  The word at workspace + 8 (int32)
+ * counts waits that were abandoned after about a second (0 unless the device
+ * stalls); it is never reset by the library.
+ */
+QSA_API int qsa_decode_fused(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq, int32_t k,
+                             float scale, int32_t num_splits, int32_t* sel_idx, int32_t* sel_cnt, void* out,
+                             int64_t out_row_stride, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace bytes of qsa_decode_fused (0 if the arguments are invalid). */
+QSA_API size_t qsa_decode_fused_workspace_bytes(const qsa_kv_t* kv, int32_t Hq, int32_t k, int32_t num_splits);
+
+/*
  * a6 -- sparse attention, extend.  Like decode, but every query row r has its
  * own sequence q_seq[r], position t = q_pos[r] and selection, and tokens
  * after t are masked: T = { 4b + u : b selected, 4b + u < L, 4b + u <= t }.

@@ -154,6 +154,60 @@ def test_workspace_size_formula():
     assert qsa.qsa_decode_workspace_bytes(B, Hq, 0) >= qsa.qsa_decode_workspace_bytes(B, Hq, 16)
 
 
+def test_fused_rejects():
+    d = kv()
+    f = qsa.lib().qsa_decode_fused
+    wsb = qsa.qsa_decode_fused_workspace_bytes(d, 16, 512, 0)
+    assert wsb > 0
+    base = [ctypes.byref(d), P, 4096, 16, 512, 0.0, 0, P, P, P, 4096, P, P, wsb, None]
+    names = ["kv", "q", "qs", "Hq", "k", "scale", "S", "sel", "cnt", "out", "os", "lse", "ws", "wb", "st"]
+
+    def call(**ch):
+        a = list(base)
+        for n, v in ch.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    assert call(k=2049) == qsa.QSA_ERR_INVALID_ARG
+    assert call(k=-1) == qsa.QSA_ERR_INVALID_ARG
+    assert call(S=65) == qsa.QSA_ERR_INVALID_ARG
+    assert call(S=-1) == qsa.QSA_ERR_INVALID_ARG
+    assert call(sel=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(cnt=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(out=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(out=P + 2) == qsa.QSA_ERR_INVALID_ARG           # out must be 8-byte aligned
+    assert call(os=100) == qsa.QSA_ERR_INVALID_ARG
+    assert call(os=4098) == qsa.QSA_ERR_INVALID_ARG              # row stride not a multiple of 4
+    assert call(q=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(ws=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(wb=wsb - 1) == qsa.QSA_ERR_INVALID_ARG
+    assert call(ws=P + 16) == qsa.QSA_ERR_INVALID_ARG            # workspace must be 256-byte aligned
+    assert call(Hq=7) == qsa.QSA_ERR_UNSUPPORTED
+    for over in (dict(v=None), dict(ckey=None), dict(k=None)):
+        dv = kv(**over)
+        assert f(ctypes.byref(dv), *base[1:]) == qsa.QSA_ERR_INVALID_ARG
+    assert qsa.qsa_last_error() != ""
+
+
+def test_fused_workspace_bytes():
+    d = kv()
+    B, Hq = 2, 16
+    auto = qsa.qsa_decode_fused_workspace_bytes(d, Hq, 512, 0)
+    s4 = qsa.qsa_decode_fused_workspace_bytes(d, Hq, 512, 4)
+    s16 = qsa.qsa_decode_fused_workspace_bytes(d, Hq, 512, 16)
+    # the partials grow with the split count: S x B x Hq x (1 KiB + 4 B)
+    assert s16 - s4 >= 12 * B * Hq * 1024
+    assert auto in (s4, s16) or auto > 0
+    assert auto % 256 == 0 and s4 % 256 == 0
+    # the scores (4 B per block of every (sequence, KV head), the row rounded up to
+    # 64 blocks) are part of it: 800 more blocks in each of the 4 rows
+    longer = qsa.qsa_decode_fused_workspace_bytes(kv(max_seq_len=6400, max_pages_per_seq=100), Hq, 512, 4)
+    assert longer - s4 >= 4 * (800 - 64) * 4
+    for args in ((Hq, -1, 0), (Hq, 2049, 0), (Hq, 512, 65), (0, 512, 0)):
+        assert qsa.qsa_decode_fused_workspace_bytes(d, *args) == 0
+    assert qsa.qsa_decode_fused_workspace_bytes(kv(batch=-1), Hq, 512, 0) == 0
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(qsa, "_lib", None)
     monkeypatch.setattr(qsa, "LIB_PATH", str(tmp_path / "libqsa.so"))

@@ -1,0 +1,199 @@
+"""The fused decode entry point (block scores, top-k, attention and merge in one
+launch) through the C ABI: its selection must equal the separate calls' bit for
+bit (the same fp32 scores decide it), and its output must meet the oracle bar
+|gpu - oracle| <= 1e-2 + 1e-2 |oracle| like the separate path.  The workspace's
+control area must be zero again after every call, with no abandoned waits."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_compress_amd as qsa
+import synth
+from block_sparse_attention_compress_amd.pipeline import FusedDecodeBuffers, decode_step_fused
+from gpu_harness import Dev, log, to_np
+from parity import check_close, check_lse
+from test_gpu_parity import check_decode_against_oracle, small_decode
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def control_bytes(units: int) -> int:
+    # ticket words (256 B), then three int32 counters per (sequence, KV head)
+    return ((256 + 12 * units + 255) // 256) * 256
+
+
+def fused(d: Dev, k=None, num_splits=0, scale=0.0, ws=None):
+    c = d.case
+    k = c.topk if k is None else k
+    q = d.t["q"]
+    sel = torch.full((c.B, c.Hkv, max(k, 1)), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((c.B, c.Hkv), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((c.B, c.Hq, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((c.B, c.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    wsb = qsa.qsa_decode_fused_workspace_bytes(d.kv, c.Hq, k, num_splits)
+    assert wsb > 0
+    if ws is None:
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    assert ws.numel() >= wsb
+    qsa.qsa_decode_fused(d.kv, q, q.stride(0), c.Hq, k, scale, num_splits, sel, cnt, out, out.stride(0), lse,
+                         workspace=ws, workspace_bytes=ws.numel())
+    torch.cuda.synchronize()
+    ctl = ws[:control_bytes(c.B * c.Hkv)]
+    assert int(torch.count_nonzero(ctl)) == 0, "control area not returned to zero"
+    return to_np(sel), to_np(cnt), to_np(out), to_np(lse)
+
+
+def check_fused(case, k=None, num_splits=0, scale=0.0):
+    """Fused vs the separate calls (selection bit-exact) and vs the oracle."""
+    k = case.topk if k is None else k
+    d = Dev(case)
+    d.compress()
+    sc = d.scores()
+    sel_ref, cnt_ref = d.topk(sc, k)
+    fsel, fcnt, fout, flse = fused(d, k=k, num_splits=num_splits, scale=scale)
+    sel_ref, cnt_ref = to_np(sel_ref), to_np(cnt_ref)
+    assert np.array_equal(fcnt, cnt_ref)
+    assert np.array_equal(fsel[:, :, :k], sel_ref[:, :, :k])
+    check_decode_against_oracle(case, d, to_np(sc), fsel, fcnt, fout, flse, k)
+    return d, fsel, fcnt, fout, flse
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (24, 2), (12, 1), (6, 1), (3, 1)])
+def test_fused_head_pairs(Hq, Hkv):
+    lens = [2051, 4097, 9000, 130]
+    case = small_decode(f"fdec{Hq}", 300 + Hq, Hq, Hkv, lens, 64, jitter=True)
+    log(f"fused heads=({Hq},{Hkv}) lens={lens}")
+    check_fused(case)
+
+
+@pytest.mark.parametrize("L,k", [(1, 1), (63, 16), (64, 16), (65, 17), (2051, 513)])
+def test_fused_selection_widths(L, k):
+    case = small_decode(f"fw{L}", 400 + L, 16, 2, [L, L], 64, topk=k)
+    log(f"fused width L={L} k={k}")
+    check_fused(case, k=k)
+
+
+@pytest.mark.parametrize("page_size", [4, 16, 256, 16384])
+def test_fused_page_sizes(page_size):
+    lens = [16384, 5000, 777] if page_size == 16384 else [7000, 5000, 777]
+    case = small_decode(f"fps{page_size}", 500 + page_size, 16, 2, lens, page_size, shuffle=page_size < 16384)
+    log(f"fused page_size={page_size} lens={lens}")
+    check_fused(case)
+
+
+@pytest.mark.parametrize("S", [1, 3, 16])
+def test_fused_explicit_splits(S):
+    case = small_decode(f"fs{S}", 600 + S, 12, 1, [9000, 3001, 4096], 64)
+    log(f"fused splits={S}")
+    check_fused(case, num_splits=S)
+
+
+@pytest.mark.parametrize("scale", [0.03125, 0.2])
+def test_fused_explicit_scale(scale):
+    case = small_decode("fscale", 9, 16, 2, [3000, 2500], 64)
+    case.scale = scale
+    check_fused(case, scale=scale)
+
+
+def test_fused_zero_k():
+    case = small_decode("fk0", 5, 16, 2, [1000, 77], 64, topk=0)
+    d = Dev(case)
+    d.compress()
+    sel, cnt, out, lse = fused(d, k=0)
+    assert np.all(cnt == 0) and np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_fused_empty_and_tiny_sequences():
+    case = small_decode("fL0", 6, 8, 2, [0, 300, 1, 3], 64)
+    d, sel, cnt, out, lse = check_fused(case)
+    assert np.all(cnt[0] == 0) and np.all(sel[0] == -1)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+def test_fused_ties_resolved_in_lds_and_in_memory():
+    """A zero query makes every score 0: one histogram bin holds every block.  With
+    1,500 blocks the bin is resolved from LDS, with 5,000 from memory; both must give
+    blocks 0..511 (the lower index wins)."""
+    case = small_decode("fq0", 8, 16, 2, [6000, 20000], 64)
+    case._q = np.zeros_like(case.q)
+    d, sel, cnt, out, lse = check_fused(case)
+    for r in range(case.R):
+        for h in range(case.Hkv):
+            assert np.array_equal(sel[r, h], np.arange(512))
+
+
+def test_fused_workspace_reused_by_a_smaller_call():
+    """Two calls on one workspace, the second with fewer sequences: both correct, and
+    the control area is zero after each (checked inside fused())."""
+    big = small_decode("fbig", 12, 16, 2, [9000, 7000, 5000, 3000], 64)
+    small = small_decode("fsmall", 13, 16, 2, [4000, 2500], 64)
+    dbig, dsmall = Dev(big), Dev(small)
+    dbig.compress()
+    dsmall.compress()
+    ws = torch.zeros(qsa.qsa_decode_fused_workspace_bytes(dbig.kv, big.Hq, big.topk, 0), dtype=torch.uint8,
+                     device="cuda")
+    for d in (dbig, dsmall, dbig):
+        sc = d.scores()
+        sel_ref, cnt_ref = d.topk(sc, d.case.topk)
+        fsel, fcnt, fout, flse = fused(d, ws=ws)
+        assert np.array_equal(fsel, to_np(sel_ref)) and np.array_equal(fcnt, to_np(cnt_ref))
+        check_decode_against_oracle(d.case, d, to_np(sc), fsel, fcnt, fout, flse, d.case.topk)
+    assert int(ws[8:12].view(torch.int32).item()) == 0, "a wait was abandoned"
+
+
+def test_fused_matches_separate_path_at_full_size():
+    """32 sequences of 32K-64K tokens, (16,2) heads, shuffled 64-token pages: the
+    benchmark's decode workload.  Selections equal the separate calls'; outputs
+    agree with theirs and with the oracle on sampled rows."""
+    case = synth.config("C2")
+    log(f"C2 fused: B={case.B} lens {int(case.lens.min())}..{int(case.lens.max())}")
+    d = Dev(case)
+    case.drop_paged()
+    d.compress()
+    sc = d.scores()
+    sel_ref, cnt_ref = d.topk(sc, case.topk)
+    out_ref, lse_ref = d.decode_attn(sel_ref, cnt_ref, case.topk)
+    fsel, fcnt, fout, flse = fused(d)
+    assert np.array_equal(fsel, to_np(sel_ref)) and np.array_equal(fcnt, to_np(cnt_ref))
+    out_ref, lse_ref = to_np(out_ref), to_np(lse_ref)
+    for r in range(case.B):
+        check_close(fout[r], out_ref[r], f"C2 fused vs separate out row {r}")
+        check_lse(flse[r], lse_ref[r], f"C2 fused vs separate lse row {r}")
+    from test_gpu_configs import compare_rows
+    compare_rows(case, [0, 13, 31], fsel, fcnt, fout, flse, d.stride)
+
+
+def test_fused_pipeline_step_and_graph_replay():
+    """decode_step_fused captured in a HIP graph: every replay equals the eager step."""
+    case = small_decode("fgraph", 14, 16, 2, [9000, 4097, 6000], 64)
+    d = Dev(case)
+    d.compress()
+    q, q_pos = d.t["q"], d.t["q_pos"]
+    buf = FusedDecodeBuffers.allocate(d.kv, case.Hq, case.topk)
+    decode_step_fused(d.kv, q, q_pos, buf, scale=case.scale)
+    torch.cuda.synchronize()
+    eager = buf.out.clone(), buf.lse.clone(), buf.sel_idx.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_step_fused(d.kv, q, q_pos, buf, scale=case.scale)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_step_fused(d.kv, q, q_pos, buf, scale=case.scale)
+    for i in range(3):
+        buf.out.fill_(0)
+        buf.lse.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(buf.sel_idx, eager[2]), i
+        assert torch.equal(buf.out, eager[0]), i
+        assert torch.equal(buf.lse, eager[1]), i
+    ctl = buf.workspace[:control_bytes(case.B * case.Hkv)]
+    assert int(torch.count_nonzero(ctl)) == 0
