@@ -46,18 +46,23 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
                       scores + ((int64_t)row * Hkv + h) * score_stride);
 }
 
-// Extend: 64 rows per workgroup, 16 per wave.  Lane (c = lane & 15, kq = lane >> 4)
-// holds, at k-step m, qsum[row c][64 kq + m] (A operand) and
-// ckey[block c][64 kq + m] (B operand): the same dim for A and B, so the 64
-// steps of the 16x16x4 matrix-core op cover all 256 dims.  Output element i of
-// the lane is row 4 kq + i, block c of the tile.  Rows of one wave that belong to
-// different sequences are scored in separate passes.
+// Extend: 64 rows per workgroup, 16 per wave, and kTiledChunk blocks per
+// workgroup (grid z), so a chunk of new tokens spreads over every CU.  Lane
+// (c = lane & 15, kq = lane >> 4) holds, at k-step m, qsum[row c][64 kq + m] (A
+// operand) and ckey[block c][64 kq + m] (B operand): the same dim for A and B, so
+// the 64 steps of the 16x16x4 matrix-core op cover all 256 dims.  Output element
+// i of the lane is row 4 kq + i, block c of the tile.  The next 16-block tile's
+// keys are loaded while the current tile is multiplied.  Rows of one wave that
+// belong to different sequences are scored in separate passes.
+constexpr int kTiledChunk = 512;
+
 __global__ __launch_bounds__(256) void scores_tiled_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int R, int g, const float* __restrict__ ckey,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages,
     float* __restrict__ scores, int score_stride) {
     const int h = blockIdx.y;
+    const int bc0 = blockIdx.z * kTiledChunk;  // this workgroup's first block
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int r0 = blockIdx.x * 64 + wave * 16;
@@ -67,11 +72,14 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
     const bool valid = row < R;
     const int seq_r = valid ? q_seq[row] : -1;
     const int t_r = valid ? q_pos[row] : -1;
+    // rows whose eligible blocks all lie before this chunk take no part
+    const bool live = valid && t_r >= 0 && min(t_r / 4 + 1, score_stride) > bc0;
+    if (!__ballot(live)) return;
 
     float a[64];
 #pragma unroll
     for (int m = 0; m < 64; ++m) a[m] = 0.f;
-    if (valid) {
+    if (live) {
         const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + 64 * kq;
         for (int j = 0; j < g; ++j) {
             const uint4* p = reinterpret_cast<const uint4*>(qrow + j * kHeadDim);
@@ -93,47 +101,52 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
         }
     }
     const int lg_bpp = lg_ps - 2;
-    const uint64_t row_lanes = __ballot(valid && kq == 0 && t_r >= 0) & 0xffffull;
-    uint64_t pending = row_lanes;
+    uint64_t pending = __ballot(live && kq == 0) & 0xffffull;
     while (pending) {
         const int first = __builtin_ctzll(pending);
         const int s = __shfl(seq_r, first);
-        const uint64_t active = __ballot(kq == 0 && valid && t_r >= 0 && seq_r == s) & 0xffffull;
+        const uint64_t active = __ballot(kq == 0 && live && seq_r == s) & 0xffffull;
         pending &= ~active;
-        const int L = seq_lens[s];
-        const int nb_seq = (L + 3) >> 2;
+        const int nb_seq = (seq_lens[s] + 3) >> 2;
         const int ne_c = ((active >> c) & 1) ? min(t_r / 4 + 1, score_stride) : 0;
-        const int n_max = wave_max_int(ne_c);
+        const int n_end = min(wave_max_int(ne_c), bc0 + kTiledChunk);
         int ne_out[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ne_out[i] = __shfl(ne_c, 4 * kq + i);
-        for (int bt0 = 0; bt0 < n_max; bt0 += 16) {
+        // block keys of the tile at bt0 into v (zeros past the sequence)
+        auto load_tile = [&](int bt0, float4* v) {
             const int b = bt0 + c;
-            float bv[64];
             if (b < nb_seq) {
                 const int64_t page = block_table[(int64_t)s * max_pages + (b >> lg_bpp)];
                 const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
                 const float4* src = reinterpret_cast<const float4*>(ckey + brow * kHeadDim + 64 * kq);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float4 w = src[i];
-                    bv[4 * i] = w.x;
-                    bv[4 * i + 1] = w.y;
-                    bv[4 * i + 2] = w.z;
-                    bv[4 * i + 3] = w.w;
-                }
+                for (int i = 0; i < 16; ++i) v[i] = src[i];
             } else {
 #pragma unroll
-                for (int m = 0; m < 64; ++m) bv[m] = 0.f;
+                for (int i = 0; i < 16; ++i) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
+        };
+        float4 cur[16], nxt[16];
+        if (bc0 < n_end) load_tile(bc0, cur);
+        for (int bt0 = bc0; bt0 < n_end; bt0 += 16) {
+            if (bt0 + 16 < n_end) load_tile(bt0 + 16, nxt);
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 64; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], bv[m], acc, 0, 0, 0);
+            for (int i = 0; i < 16; ++i) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 0], cur[i].x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 1], cur[i].y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 2], cur[i].z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 3], cur[i].w, acc, 0, 0, 0);
+            }
+            const int b = bt0 + c;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = 4 * kq + i;
                 if (b < ne_out[i]) scores[((int64_t)(r0 + rr) * Hkv + h) * score_stride + b] = acc[i];
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
         }
     }
 }
@@ -156,7 +169,7 @@ hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scor
 hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
                                hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
-    dim3 grid((rows.R + 63) / 64, kv.Hkv);
+    dim3 grid((rows.R + 63) / 64, kv.Hkv, (score_stride + kTiledChunk - 1) / kTiledChunk);
     hipLaunchKernelGGL(scores_tiled_kernel, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq, rows.q_pos,
                        rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,
                        kv.max_pages, scores, score_stride);
