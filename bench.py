@@ -211,7 +211,7 @@ def main():
     log(f"inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
     kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
     q, q_pos = dev["q"], dev["q_pos"]
-    stride = max(case.nb(i) for i in range(case.B))
+    stride = (max(case.nb(i) for i in range(case.B)) + 63) // 64 * 64  # 16-byte rows for the selection's loads
     buf = DecodeBuffers.allocate(case.B, case.Hq, case.Hkv, stride, case.topk, 0, "cuda")
 
     # full block-key build (prefill-time work, timed on its own)

@@ -11,8 +11,9 @@
 // with key == T.  The result does not depend on thread timing.
 //
 // topk_reg_kernel (rows of up to 65,536 blocks): one 1024-thread workgroup per
-// (row, KV head); the row lives in registers (KPT scores per thread, block
-// t + 1024 j in thread t).  Radix digits of raw float keys crowd into a few
+// (row, KV head); the row lives in registers (KPT scores per thread, thread t
+// holding blocks t KPT .. t KPT + KPT - 1, so thread order is block order and
+// one prefix sum of per-thread counts places the output).  Radix digits of raw float keys crowd into a few
 // exponent bins, and LDS atomics on one address serialise, so the first pass
 // bins uniformly between the row's min and max instead: any monotonic binning
 // keeps the selection exact.  The bin holding the k-th value is then resolved
@@ -89,7 +90,6 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     __shared__ int hist[kBins];
     __shared__ float cand_val[kRegThreads];
     __shared__ int cand_idx[kRegThreads];
-    __shared__ int cnt_gt[KPT * kRegWaves], cnt_eq[KPT * kRegWaves];
     __shared__ int itmp[2 * kRegWaves];
     __shared__ float ftmp[64];
     __shared__ int sh_bin, sh_above, sh_ncand, sh_need_eq;
@@ -103,27 +103,39 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     if (topk_trivial(n, k, out, sel_cnt + unit)) return;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int i0 = tid * KPT;  // this thread's first block
     const float* s = scores + (int64_t)unit * score_stride;
     // slots past n hold -inf (scores are finite): it is never selected, and
     // every test below stays a function of the value (no per-slot masks kept live)
     float v[KR];
+    auto put = [&](int e, float raw) {
+        const float x = i0 + e < n ? raw + 0.0f : -INFINITY;  // + 0 turns -0 into +0
+        if (e < KR) v[e < KR ? e : 0] = x;
+        else vl[(e - KR) * kRegThreads + tid] = x;
+    };
+    if (KPT >= 4 && (score_stride & 3) == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
+        // float4 loads, clamped and unconditional, so all KPT / 4 are in flight at once
+        // (a whole float4 lies inside the row: n4 <= score_stride / 4)
+        const float4* s4 = reinterpret_cast<const float4*>(s);
+        const int n4 = (n + 3) / 4;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int i = tid + kRegThreads * j;
-        // unconditional (clamped) loads, so all KPT are in flight at once
-        const float raw = s[min(i, n - 1)];
-        const float x = i < n ? raw + 0.0f : -INFINITY;  // + 0 turns -0 into +0
-        if (j < KR) v[j < KR ? j : 0] = x;
-        else vl[(j - KR) * kRegThreads + tid] = x;
+        for (int j = 0; j < (KPT >= 4 ? KPT / 4 : 1); ++j) {
+            const float4 x = s4[min(i0 / 4 + j, n4 - 1)];
+            put(4 * j + 0, x.x);
+            put(4 * j + 1, x.y);
+            put(4 * j + 2, x.z);
+            put(4 * j + 3, x.w);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) put(e, s[min(i0 + e, n - 1)]);
     }
-    auto V = [&](int j) -> float { return j < KR ? v[j < KR ? j : 0] : vl[(j - KR) * kRegThreads + tid]; };
+    auto V = [&](int e) -> float { return e < KR ? v[e < KR ? e : 0] : vl[(e - KR) * kRegThreads + tid]; };
     float mn = FLT_MAX, mx = -FLT_MAX;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        mn = fminf(mn, V(j) == -INFINITY ? FLT_MAX : V(j));
-        mx = fmaxf(mx, V(j));
+    for (int e = 0; e < KPT; ++e) {
+        mn = fminf(mn, V(e) == -INFINITY ? FLT_MAX : V(e));
+        mx = fmaxf(mx, V(e));
     }
     const float range = block_min_max(mn, mx, ftmp);
     if (range == 0.f) {  // every score equal: the k lowest indices
@@ -140,8 +152,8 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     for (int i = tid; i < kBins; i += kRegThreads) hist[i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-        if (V(j) != -INFINITY) atomicAdd(&hist[bin_of(V(j))], 1);
+    for (int e = 0; e < KPT; ++e)
+        if (V(e) != -INFINITY) atomicAdd(&hist[bin_of(V(e))], 1);
     __syncthreads();
     {
         const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
@@ -166,11 +178,11 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     if (m <= kRegThreads) {
         // ---- rank the bin's candidates directly
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            if (V(j) != -INFINITY && bin_of(V(j)) == B) {
+        for (int e = 0; e < KPT; ++e) {
+            if (V(e) != -INFINITY && bin_of(V(e)) == B) {
                 const int slot = atomicAdd(&sh_ncand, 1);
-                cand_val[slot] = V(j);
-                cand_idx[slot] = tid + kRegThreads * j;
+                cand_val[slot] = V(e);
+                cand_idx[slot] = i0 + e;
             }
         }
         __syncthreads();
@@ -201,9 +213,9 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
             for (int i = tid; i < kBins; i += kRegThreads) hist[i] = 0;
             __syncthreads();
 #pragma unroll
-            for (int j = 0; j < KPT; ++j) {
-                const uint32_t key = order_key(V(j));
-                if (V(j) != -INFINITY && bin_of(V(j)) == B && (key & mask) == prefix)
+            for (int e = 0; e < KPT; ++e) {
+                const uint32_t key = order_key(V(e));
+                if (V(e) != -INFINITY && bin_of(V(e)) == B && (key & mask) == prefix)
                     atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
             }
             __syncthreads();
@@ -234,44 +246,28 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     const uint32_t T = sh_T;
     const int need_eq = sh_need_eq;
 
-    // ---- ordered compaction: element t + 1024 j comes after all of rows < j and
-    // after the lower threads of row j
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    // ---- ordered compaction: thread order is block order, so per-thread counts
+    // and one prefix sum place every selected block
+    int gt = 0, eq = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const uint32_t key = order_key(V(j));
-        const uint64_t g = __ballot(key > T);
-        const uint64_t e = __ballot(key == T);
-        if (lane == 0) {
-            cnt_gt[j * kRegWaves + wave] = __popcll(g);
-            cnt_eq[j * kRegWaves + wave] = __popcll(e);
-        }
+    for (int e = 0; e < KPT; ++e) {
+        const uint32_t key = order_key(V(e));
+        const bool real = V(e) != -INFINITY;
+        gt += real && key > T;
+        eq += real && key == T;
     }
-    __syncthreads();
-    {
-        int a = tid < KPT * kRegWaves ? cnt_gt[tid] : 0;
-        int b = tid < KPT * kRegWaves ? cnt_eq[tid] : 0;
-        block_exclusive_scan2<kRegWaves>(a, b, itmp);
-        if (tid < KPT * kRegWaves) {
-            cnt_gt[tid] = a;
-            cnt_eq[tid] = b;
-        }
-    }
-    __syncthreads();
+    block_exclusive_scan2<kRegWaves>(gt, eq, itmp);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int i = tid + kRegThreads * j;
-        const uint32_t key = order_key(V(j));
-        const bool is_gt = key > T;
-        const bool is_eq = key == T;
-        const uint64_t g = __ballot(is_gt);
-        const uint64_t e = __ballot(is_eq);
-        const int gt_before = cnt_gt[j * kRegWaves + wave] + __popcll(g & below);
-        const int eq_before = cnt_eq[j * kRegWaves + wave] + __popcll(e & below);
-        int pos = -1;
-        if (is_gt) pos = gt_before + min(eq_before, need_eq);
-        if (is_eq && eq_before < need_eq) pos = gt_before + eq_before;
-        if (pos >= 0 && pos < k) out[pos] = i;
+    for (int e = 0; e < KPT; ++e) {
+        if (V(e) == -INFINITY) continue;
+        const uint32_t key = order_key(V(e));
+        if (key > T) {
+            out[gt + min(eq, need_eq)] = i0 + e;
+            ++gt;
+        } else if (key == T) {
+            if (eq < need_eq) out[gt + eq] = i0 + e;
+            ++eq;
+        }
     }
     if (tid == 0) sel_cnt[unit] = k;
 }

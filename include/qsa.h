@@ -133,7 +133,9 @@ QSA_API int qsa_block_scores(const qsa_kv_t* kv, const void* q, int64_t q_row_st
  * ascending; -0 equals +0), and writes them in ascending block order to
  *   sel_idx[(r * Hkv + h) * k + j], j < cnt, then -1 up to k,
  *   sel_cnt[r * Hkv + h] = cnt = min(k, n_elig(r)).
- * 0 <= k <= QSA_MAX_TOPK.  Scores must be finite.
+ * 0 <= k <= QSA_MAX_TOPK.  Scores must be finite.  Rows are read with 16-byte
+ * loads when score_stride is a multiple of 4 and scores is 16-byte aligned
+ * (any stride works).
  */
 QSA_API int qsa_topk_blocks(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R, int32_t Hkv,
                     int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* stream);

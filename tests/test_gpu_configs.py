@@ -66,7 +66,7 @@ def decode_full(name, sample, num_splits=0):
     log(f"{name}: B={case.B} lens {int(case.lens.min())}..{int(case.lens.max())} heads ({case.Hq},{case.Hkv})")
     dev, kv = upload(case)
     qsa.qsa_compress_keys(kv)
-    stride = max(case.nb(i) for i in range(case.B))
+    stride = (max(case.nb(i) for i in range(case.B)) + 63) // 64 * 64  # as the benchmark
     buf = DecodeBuffers.allocate(case.B, case.Hq, case.Hkv, stride, case.topk, num_splits, "cuda")
     decode_step(kv, dev["q"], dev["q_pos"], buf, scale=case.scale, num_splits=num_splits)
     torch.cuda.synchronize()
@@ -101,7 +101,7 @@ def test_c5_split4_merge_equals_unsplit():
     log(f"C5: B={case.B} lens {int(case.lens.min())}..{int(case.lens.max())}")
     dev, kv = upload(case)
     qsa.qsa_compress_keys(kv)
-    stride = max(case.nb(i) for i in range(case.B))
+    stride = (max(case.nb(i) for i in range(case.B)) + 63) // 64 * 64  # as the benchmark
     buf = DecodeBuffers.allocate(case.B, case.Hq, case.Hkv, stride, case.topk, 4, "cuda")
     decode_step(kv, dev["q"], dev["q_pos"], buf, scale=case.scale, num_splits=4)
     # the same selection: explicit partials + merge, and unsplit
