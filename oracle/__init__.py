@@ -60,6 +60,7 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         L.oracle_compress.argtypes = [vp, i64, i32, vp]
+        L.oracle_compress_bf16.argtypes = [vp, i64, i32, vp]
         L.oracle_scores.argtypes = [vp, i32, i32, vp, i64, vp]
         L.oracle_topk.argtypes = [vp, i64, i32, vp, vp]
         L.oracle_attend.argtypes = [vp, i32, i32, vp, vp, i64, i64, vp, i32, dbl, i32, i32, vp, vp]
@@ -82,12 +83,17 @@ def _check(rc: int, what: str):
 
 # ----------------------------------------------------------------------- steps
 
-def compress(keys: np.ndarray) -> np.ndarray:
-    """keys bf16 bits [L][D] -> block keys float32 [ceil(L/4)][D]."""
+def compress(keys: np.ndarray, ckey_dtype: str = "fp32") -> np.ndarray:
+    """keys bf16 bits [L][D] -> block keys float32 [ceil(L/4)][D]; with
+    ckey_dtype "bf16", the fp32 means rounded to bf16 (returned as float32)."""
     keys = np.ascontiguousarray(keys, dtype=np.uint16)
     L, D = keys.shape
     out = np.empty(((L + 3) // 4, D), dtype=np.float32)
-    _check(lib().oracle_compress(_p(keys), L, D, _p(out)), "oracle_compress")
+    if ckey_dtype == "bf16":
+        _check(lib().oracle_compress_bf16(_p(keys), L, D, _p(out)), "oracle_compress_bf16")
+    else:
+        assert ckey_dtype == "fp32", ckey_dtype
+        _check(lib().oracle_compress(_p(keys), L, D, _p(out)), "oracle_compress")
     return out
 
 
@@ -186,7 +192,7 @@ class CaseData:
 
     def ckey(self, i: int, h: int) -> np.ndarray:
         if (i, h) not in self._ckey:
-            self._ckey[(i, h)] = compress(self.K(i)[h])
+            self._ckey[(i, h)] = compress(self.K(i)[h], self.case.ckey_dtype)
         return self._ckey[(i, h)]
 
     def prefetch(self, seqs, threads: int):
@@ -196,7 +202,8 @@ class CaseData:
             self.K(i)
         units = [(i, h) for i in seqs for h in range(self.case.Hkv) if (i, h) not in self._ckey]
         with ThreadPoolExecutor(max_workers=threads) as ex:
-            for (i, h), ck in zip(units, ex.map(lambda u: compress(self.K(u[0])[u[1]]), units)):
+            for (i, h), ck in zip(units, ex.map(lambda u: compress(self.K(u[0])[u[1]], self.case.ckey_dtype),
+                                                units)):
                 self._ckey[(i, h)] = ck
 
     def release(self, i: int):

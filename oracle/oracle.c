@@ -78,6 +78,34 @@ int oracle_compress(const uint16_t* keys, int64_t L, int32_t D, float* ckey) {
     return 0;
 }
 
+/* ------------------------------------------------------------------ O1b
+ * Reduced-precision block keys.  The pages record smaller cache formats for
+ * this attention path (an FP8 main KV cache for the sparse-attention path, in
+ * "Pengambilan sampel batch-sharded Qwen4Exp: di dalam vLLM PR #61018, dan apa
+ * yang dikatakannya tentang Qwen 4", section "Apa yang dikatakan oleh klaster
+ * patch di sekitarnya tentang Qwen4Exp"); the library's variant stores block
+ * keys in bf16.  A bf16 block key is the O1 fp32 mean rounded to the nearest
+ * bf16 value, ties to the even one.  It is returned widened to fp32 (exact), so
+ * O2 applies unchanged. */
+static float round_to_bf16(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    /* finite inputs: add half an ulp of bf16, plus one if the kept part is odd */
+    const uint32_t keep_odd = (u >> 16) & 1u;
+    u = (u + 0x7fffu + keep_odd) & 0xffff0000u;
+    float r;
+    memcpy(&r, &u, 4);
+    return r;
+}
+
+int oracle_compress_bf16(const uint16_t* keys, int64_t L, int32_t D, float* ckey) {
+    int rc = oracle_compress(keys, L, D, ckey);
+    if (rc) return rc;
+    const int64_t nb = (L + 3) / 4;
+    for (int64_t i = 0; i < nb * D; ++i) ckey[i] = round_to_bf16(ckey[i]);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ O2
  * Block scores of one (row, KV head): q [g][D] bf16 holds the g query heads
  * of the group; s[b] = sum_d (sum_j q[j][d]) * ckey[b][d] for b < n_elig,

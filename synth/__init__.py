@@ -143,6 +143,7 @@ class Case:
     bias_mag: float = 3.0
     shuffle: bool = True
     shared_prefix_pages: int = 0     # sequence i>0 reuses the first pages of sequence 0
+    ckey_dtype: str = "fp32"         # storage of the block keys: "fp32" or "bf16"
     block_table: np.ndarray = field(default=None, repr=False)   # int32 [B][max_pages]
     num_pages: int = 0
     _q: Optional[np.ndarray] = field(default=None, repr=False)
@@ -254,7 +255,8 @@ class Case:
 def to_device(case: Case, device="cuda", ckey: bool = True):
     """Upload a case's paged pool, tables and queries as torch tensors (layout only).
 
-    Returns a dict: k, v (bf16 [num_pages][Hkv][page_size][D]), ckey (fp32, zeroed),
+    Returns a dict: k, v (bf16 [num_pages][Hkv][page_size][D]), ckey (fp32 or bf16 as the
+    case stores block keys, zeroed),
     block_table, seq_lens, q_seq, q_pos (int32), q (bf16 [R][Hq][D])."""
     import torch
 
@@ -271,8 +273,8 @@ def to_device(case: Case, device="cuda", ckey: bool = True):
         "q": bf16(case.q),
     }
     if ckey:
-        out["ckey"] = torch.zeros((case.num_pages, case.Hkv, case.page_size // 4, case.D), dtype=torch.float32,
-                                  device=device)
+        dt = torch.bfloat16 if case.ckey_dtype == "bf16" else torch.float32
+        out["ckey"] = torch.zeros((case.num_pages, case.Hkv, case.page_size // 4, case.D), dtype=dt, device=device)
     return out
 
 
@@ -301,7 +303,8 @@ def _block_table(seed: int, lens: np.ndarray, page_size: int, shuffle: bool, sha
 
 def make_case(name: str, seed: int, Hq: int, Hkv: int, lens, page_size: int, *, q_seq=None, q_pos=None,
               topk: int = 512, scale: float = 1.0 / 16.0, splits: int = 1, jitter: bool = False,
-              bias_frac: float = 0.0, shuffle: bool = True, shared_prefix_pages: int = 0, D: int = 256) -> Case:
+              bias_frac: float = 0.0, shuffle: bool = True, shared_prefix_pages: int = 0, D: int = 256,
+              ckey_dtype: str = "fp32") -> Case:
     lens = np.asarray(lens, dtype=np.int32)
     if q_seq is None:  # decode: one row per sequence at its last position
         q_seq = np.arange(lens.shape[0], dtype=np.int32)
@@ -310,7 +313,7 @@ def make_case(name: str, seed: int, Hq: int, Hkv: int, lens, page_size: int, *, 
     return Case(name=name, seed=seed, Hq=Hq, Hkv=Hkv, lens=lens, page_size=page_size,
                 q_seq=np.asarray(q_seq, dtype=np.int32), q_pos=np.asarray(q_pos, dtype=np.int32), topk=topk,
                 scale=scale, splits=splits, D=D, jitter=jitter, bias_frac=bias_frac, shuffle=shuffle,
-                shared_prefix_pages=shared_prefix_pages, block_table=bt, num_pages=num_pages)
+                shared_prefix_pages=shared_prefix_pages, block_table=bt, num_pages=num_pages, ckey_dtype=ckey_dtype)
 
 
 def uniform_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:

@@ -105,6 +105,41 @@ def test_o1_tail_divisor_three():
 
 # --------------------------------------------------------------------------- O2
 
+def test_o1b_bf16_block_keys_match_torch_rounding():
+    """O1b: the bf16 block key is the O1 mean rounded to nearest bf16, ties to even.
+    Pinned against torch's own float32 -> bfloat16 conversion (catches truncation
+    instead of rounding, or rounding the keys before the mean)."""
+    for L in (64, 61, 7, 1):
+        keys = rand_bf16((L, 256), scale=3.0)
+        mean = oracle.compress(keys)
+        want = torch.from_numpy(mean).to(torch.bfloat16).to(torch.float32).numpy()
+        got = oracle.compress(keys, "bf16")
+        assert got.dtype == np.float32 and got.shape == mean.shape
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), L
+
+
+def test_o1b_ties_go_to_even_and_exact_means_stay():
+    """O1b closed forms: a mean already in bf16 is kept; a mean exactly halfway
+    between two bf16 values goes to the one with the even last bit (catches
+    round-half-up)."""
+    u = 2.0 ** -7  # bf16 spacing on [1, 2)
+
+    def block(vals):
+        keys = np.zeros((4, 256), dtype=np.float32)
+        keys[:, 0] = vals
+        keys[:, 1] = [3.0, 3.0, 3.0, 3.0]
+        return oracle.compress(f32_to_bf16(keys), "bf16")[0]
+
+    ck = block([1.0, 1.0, 1.0 + u, 1.0 + u])            # mean 1 + u/2: tie -> 1 (even)
+    assert ck[0] == np.float32(1.0) and ck[1] == np.float32(3.0)
+    ck = block([1.0 + u, 1.0 + u, 1.0 + 2 * u, 1.0 + 2 * u])  # mean 1 + 3u/2: tie -> 1 + 2u (even)
+    assert ck[0] == np.float32(1.0 + 2 * u)
+    ck = block([1.0, 1.0, 1.0, 1.0 + u])                 # mean 1 + u/4: below the tie -> 1
+    assert ck[0] == np.float32(1.0)
+    ck = block([1.0, 1.0 + u, 1.0 + u, 1.0 + u])         # mean 1 + 3u/4: above the tie -> 1 + u
+    assert ck[0] == np.float32(1.0 + u)
+
+
 def test_o2_zero_query_and_unit_query():
     """Zero q gives all-zero scores; q = e_d in one head of the group gives the d-th
     component of each block key.  Catches a transposed operand or a scale applied."""
