@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--graph", action="store_true", help="time a replayed HIP graph of the step instead of eager launches")
     p.add_argument("--splits", type=int, default=None, help="decode split count (default: the library's choice)")
     p.add_argument("--no-fused", action="store_true", help="skip the single-launch fused step figures")
+    p.add_argument("--ckey", choices=["fp32", "bf16"], default="fp32",
+                   help="block-key storage (fp32: the method's definition; bf16: the rounded-mean variant)")
     return p.parse_args()
 
 
@@ -75,6 +77,8 @@ def describe(case) -> str:
         extra.append(f"{case.bias_frac:.0%} of microblocks biased +{case.bias_mag:g} sigma toward the query")
     if case.splits > 1:
         extra.append(f"{case.splits} split-KV partitions merged by log-sum-exp")
+    if case.ckey_dtype == "bf16":
+        extra.append("bf16 block keys (fp32 means rounded to nearest even)")
     return (f"{case.name}: decode, {case.B} sequence{'s' if case.B > 1 else ''}, {lens}, ({case.Hq},{case.Hkv}) heads, "
             f"head_dim 256, {cache}, top-{case.topk} microblocks of 4" + "".join("; " + e for e in extra))
 
@@ -102,7 +106,8 @@ def copy_calibration():
 def decode_bytes(case, sel, cnt, page_size):
     """Algorithmic HBM bytes of one decode step, and of its block-score launch.
 
-    step: per (sequence, KV head) the fp32 block-key scan (nb * 1 KiB) and the
+    step: per (sequence, KV head) the block-key scan (nb * 1 KiB for fp32 keys,
+    nb * 512 B for bf16 keys) and the
     bf16 K and V rows of the selected tokens (512 B each), plus q and out rows
     (bf16), lse (fp32), the block table and the lengths.
     scores launch: the block-key scan, the q rows, the score writes (4 B per block)
@@ -111,7 +116,7 @@ def decode_bytes(case, sel, cnt, page_size):
 
     B, Hkv, Hq = case.B, case.Hkv, case.Hq
     nb = np.array([case.nb(i) for i in range(B)], dtype=np.int64)
-    ckey = int(nb.sum()) * Hkv * 256 * 4
+    ckey = int(nb.sum()) * Hkv * 256 * (2 if case.ckey_dtype == "bf16" else 4)
     tokens = 0
     for i in range(B):
         L = int(case.lens[i])
@@ -203,6 +208,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     qsa.lib()
     case = synth.config(args.config)
+    case.ckey_dtype = args.ckey
     log(f"workload {case.name}: B={case.B} lens {int(case.lens.min())}..{int(case.lens.max())} "
         f"heads ({case.Hq},{case.Hkv}) page {case.page_size}")
     t0 = time.perf_counter()
@@ -306,7 +312,8 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("source_sha256_16") == source_hash(SCORES_SRC) and rec.get("workload") == case.name:
+        if (rec.get("source_sha256_16") == source_hash(SCORES_SRC) and rec.get("workload") == case.name
+                and rec.get("ckey_dtype", "fp32") == case.ckey_dtype):
             traffic = rec.get("hbm_bytes_per_launch")
 
     result = {

@@ -33,6 +33,8 @@ MICROBLOCK = 4
 DEFAULT_TOPK = 512
 MAX_TOPK = 2048
 MAX_SPLITS = 64
+CKEY_FP32 = 0
+CKEY_BF16 = 1
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks",
            "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse",
@@ -59,6 +61,7 @@ class qsa_kv_t(ctypes.Structure):
         ("num_pages", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int32),
+        ("ckey_dtype", ctypes.c_int32),
     ]
 
 
@@ -120,7 +123,8 @@ def _stream(stream) -> Optional[int]:
 class KVCache:
     """A paged cache as torch tensors (device memory owned by the caller).
 
-    k, v: bf16 [num_pages][Hkv][page_size][256]; ckey: fp32 [num_pages][Hkv][page_size/4][256];
+    k, v: bf16 [num_pages][Hkv][page_size][256]; ckey: fp32 or bf16 [num_pages][Hkv][page_size/4][256]
+    (its dtype selects the block-key format);
     block_table: int32 [batch][max_pages]; seq_lens: int32 [batch]; max_seq_len: host bound."""
 
     k: object
@@ -132,9 +136,10 @@ class KVCache:
 
     def descriptor(self) -> qsa_kv_t:
         num_pages, hkv, page_size, d = self.k.shape
+        bf16 = self.ckey is not None and str(getattr(self.ckey, "dtype", "")) == "torch.bfloat16"
         return qsa_kv_t(_ptr(self.k), _ptr(self.v), _ptr(self.ckey), _ptr(self.block_table), _ptr(self.seq_lens),
                         int(self.block_table.shape[0]), int(hkv), int(d), int(page_size), int(num_pages),
-                        int(self.block_table.shape[1]), int(self.max_seq_len))
+                        int(self.block_table.shape[1]), int(self.max_seq_len), CKEY_BF16 if bf16 else CKEY_FP32)
 
 
 def _kv(kv) -> qsa_kv_t:

@@ -11,14 +11,16 @@
 // one holding first_token, so a decode refresh launches one chunk per
 // (sequence, KV head).  Thread t handles
 // microblock t/16 of the chunk and dims 16*(t%16) .. +15: four 32-byte key reads,
-// one 64-byte block-key write.  A pure HBM stream (read 2 B, write 1 B per key
-// element of a block).
+// one 64-byte block-key write (32 bytes for bf16 block keys, which store the
+// same mean rounded to nearest, ties to even).  A pure HBM stream (read 2 B,
+// write 1 B -- 0.5 B for bf16 -- per key element of a block).
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
 namespace qsa {
 
-__global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restrict__ k, float* __restrict__ ckey,
+template <bool BF16>
+__global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restrict__ k, void* __restrict__ ckey,
                                                        const int32_t* __restrict__ block_table,
                                                        const int32_t* __restrict__ seq_lens,
                                                        const int32_t* __restrict__ first_token, int Hkv, int lg_ps,
@@ -80,9 +82,17 @@ __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restric
     }
     // block-key row in [num_pages][Hkv][page_size / 4][256]
     const int64_t brow = ((row >> lg_ps) << (lg_ps - 2)) + ((row & ((1 << lg_ps) - 1)) >> 2);
-    float4* dst = reinterpret_cast<float4*>(ckey + brow * kHeadDim + 16 * e);
+    if (BF16) {
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ckey) + brow * kHeadDim + 16 * e);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_float4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
+        for (int i = 0; i < 2; ++i)
+            dst[i] = make_uint4(pack_bf16x2(r[8 * i], r[8 * i + 1]), pack_bf16x2(r[8 * i + 2], r[8 * i + 3]),
+                                pack_bf16x2(r[8 * i + 4], r[8 * i + 5]), pack_bf16x2(r[8 * i + 6], r[8 * i + 7]));
+    } else {
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(ckey) + brow * kHeadDim + 16 * e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = make_float4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
+    }
 }
 
 hipError_t launch_compress(const PagedKV& kv, const int32_t* first_token, int span, hipStream_t st) {
@@ -90,8 +100,12 @@ hipError_t launch_compress(const PagedKV& kv, const int32_t* first_token, int sp
     // tokens [first, first + span) touch at most ceil(span / 64) + 1 chunks
     const int chunks = first_token ? (span + 63) / 64 + 1 : (kv.max_seq_len + 63) / 64;
     dim3 grid(chunks, kv.Hkv, kv.batch);
-    hipLaunchKernelGGL(compress_kernel, grid, dim3(256), 0, st, kv.k, kv.ckey, kv.block_table, kv.seq_lens,
-                       first_token, kv.Hkv, kv.lg_ps, kv.max_pages);
+    if (kv.ckey_bf16)
+        hipLaunchKernelGGL(compress_kernel<true>, grid, dim3(256), 0, st, kv.k, kv.ckey, kv.block_table, kv.seq_lens,
+                           first_token, kv.Hkv, kv.lg_ps, kv.max_pages);
+    else
+        hipLaunchKernelGGL(compress_kernel<false>, grid, dim3(256), 0, st, kv.k, kv.ckey, kv.block_table,
+                           kv.seq_lens, first_token, kv.Hkv, kv.lg_ps, kv.max_pages);
     return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@ namespace qsa {
 struct PagedKV {
     const uint16_t* k;
     const uint16_t* v;
-    float* ckey;
+    void* ckey;               // fp32 or bf16 block keys (ckey_bf16)
+    int ckey_bf16;
     const int32_t* block_table;
     const int32_t* seq_lens;
     int batch, Hkv, lg_ps, num_pages, max_pages, max_seq_len;

@@ -23,10 +23,28 @@ constexpr int kGroups = kStreamChunk / 64;  // 16-block groups per wave
 // past the row end are still inside the page; their sums are never written).
 // COHERENT: scores are stored at device scope (written through to where every
 // CU reads them), for a reader in another workgroup of the same launch.
-template <bool PAGE16, bool COHERENT = false>
-__device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int g, const float* __restrict__ ckey,
+// BF16: block keys are bf16 (8 bytes per lane and block instead of 16); they
+// are kept raw until the dot product, so the next group's loads still fly
+// while a group is reduced.
+template <bool BF16>
+struct KeyRaw {
+    typedef float4 type;
+};
+template <>
+struct KeyRaw<true> {
+    typedef uint2 type;
+};
+__device__ __forceinline__ float4 key4(const float4& x) { return x; }
+__device__ __forceinline__ float4 key4(const uint2& x) {
+    return make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
+}
+
+template <bool PAGE16, bool COHERENT = false, bool BF16 = false>
+__device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int g, const void* __restrict__ ckey,
                                           const int32_t* __restrict__ bt, int Hkv, int h, int lg_ps, int n_elig,
                                           int wb0, int lane, float* __restrict__ srow) {
+    typedef typename KeyRaw<BF16>::type Raw;
+    const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
     const int lg_bpp = lg_ps - 2;  // blocks per page = page_size / 4
     // block-key rows of the wave's groups (PAGE16), looked up before any wait
     int64_t gbase[kGroups];
@@ -38,24 +56,24 @@ __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int
         }
     }
 
-    auto load_group = [&](int grp, float4* v) {
+    auto load_group = [&](int grp, Raw* v) {
         const int b0 = wb0 + grp * 16;
         if (PAGE16) {
-            const float* src = ckey + gbase[grp] * kHeadDim + 4 * lane;
+            const Raw* src = keys + gbase[grp] * (kHeadDim / 4) + lane;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = *reinterpret_cast<const float4*>(src + j * kHeadDim);
+            for (int j = 0; j < 16; ++j) v[j] = src[j * (kHeadDim / 4)];
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int b = min(b0 + j, n_elig - 1);
                 const int64_t page = bt[b >> lg_bpp];
                 const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
-                v[j] = *reinterpret_cast<const float4*>(ckey + brow * kHeadDim + 4 * lane);
+                v[j] = keys[brow * (kHeadDim / 4) + lane];
             }
         }
     };
     // the first group's block keys are requested before the query
-    float4 v[16];
+    Raw v[16];
     load_group(0, v);
 
     // group-summed query: lane holds dims 4*lane .. 4*lane+3; the g loads are
@@ -80,7 +98,10 @@ __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int
         if (b0 >= n_elig) break;
         float p[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] = qs.x * v[j].x + qs.y * v[j].y + qs.z * v[j].z + qs.w * v[j].w;
+        for (int j = 0; j < 16; ++j) {
+            const float4 kv = key4(v[j]);
+            p[j] = qs.x * kv.x + qs.y * kv.y + qs.z * kv.z + qs.w * kv.w;
+        }
         // the next group's loads fly while this group is reduced
         if (grp < kGroups - 1 && b0 + 16 < n_elig) load_group(grp + 1, v);
         // reduce-scatter: after the step across lane bit m (m = 5, 4, 3, 2) a lane

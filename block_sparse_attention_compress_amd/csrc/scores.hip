@@ -22,10 +22,10 @@
 
 namespace qsa {
 
-template <bool PAGE16>
+template <bool PAGE16, bool BF16>
 __global__ __launch_bounds__(256) void scores_stream_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int g, const float* __restrict__ ckey, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ q_pos, int g, const void* __restrict__ ckey, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages, float* __restrict__ scores,
     int score_stride) {
     const int row = blockIdx.z;
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
     const int wave = wave_id();
     const int wb0 = chunk0 + wave * (kStreamChunk / 4);  // this wave's first block
     if (wb0 >= n_elig) return;
-    scan_wave<PAGE16>(q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim, g, ckey,
+    scan_wave<PAGE16, false, BF16>(q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim, g, ckey,
                       block_table + (int64_t)seq * max_pages, Hkv, h, lg_ps, n_elig, wb0, lane,
                       scores + ((int64_t)row * Hkv + h) * score_stride);
 }
@@ -56,9 +56,10 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
 // belong to different sequences are scored in separate passes.
 constexpr int kTiledChunk = 512;
 
+template <bool BF16>
 __global__ __launch_bounds__(256) void scores_tiled_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int R, int g, const float* __restrict__ ckey,
+    const int32_t* __restrict__ q_pos, int R, int g, const void* __restrict__ ckey,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages,
     float* __restrict__ scores, int score_stride) {
     const int h = blockIdx.y;
@@ -113,31 +114,34 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
         int ne_out[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ne_out[i] = __shfl(ne_c, 4 * kq + i);
-        // block keys of the tile at bt0 into v (zeros past the sequence)
-        auto load_tile = [&](int bt0, float4* v) {
+        // block keys of the tile at bt0 into v, raw (zeros past the sequence)
+        typedef typename KeyRaw<BF16>::type Raw;
+        const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
+        auto load_tile = [&](int bt0, Raw* v) {
             const int b = bt0 + c;
             if (b < nb_seq) {
                 const int64_t page = block_table[(int64_t)s * max_pages + (b >> lg_bpp)];
                 const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
-                const float4* src = reinterpret_cast<const float4*>(ckey + brow * kHeadDim + 64 * kq);
+                const Raw* src = keys + brow * (kHeadDim / 4) + 16 * kq;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[i] = src[i];
             } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int i = 0; i < 16; ++i) v[i] = Raw{};
             }
         };
-        float4 cur[16], nxt[16];
+        Raw cur[16], nxt[16];
         if (bc0 < n_end) load_tile(bc0, cur);
         for (int bt0 = bc0; bt0 < n_end; bt0 += 16) {
             if (bt0 + 16 < n_end) load_tile(bt0 + 16, nxt);
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 0], cur[i].x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 1], cur[i].y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 2], cur[i].z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 3], cur[i].w, acc, 0, 0, 0);
+                const float4 kv = key4(cur[i]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 0], kv.x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 1], kv.y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 2], kv.z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 3], kv.w, acc, 0, 0, 0);
             }
             const int b = bt0 + c;
 #pragma unroll
@@ -155,14 +159,20 @@ hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scor
                                 hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
     dim3 grid((score_stride + kStreamChunk - 1) / kStreamChunk, kv.Hkv, rows.R);
-    if (kv.lg_ps >= 6)
-        hipLaunchKernelGGL(scores_stream_kernel<true>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,
-                           rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,
-                           kv.max_pages, scores, score_stride);
+    const bool page16 = kv.lg_ps >= 6;
+#define QSA_SCAN(P16, B16)                                                                                      \
+    hipLaunchKernelGGL((scores_stream_kernel<P16, B16>), grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq, \
+                       rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,     \
+                       kv.max_pages, scores, score_stride)
+    if (page16 && kv.ckey_bf16)
+        QSA_SCAN(true, true);
+    else if (page16)
+        QSA_SCAN(true, false);
+    else if (kv.ckey_bf16)
+        QSA_SCAN(false, true);
     else
-        hipLaunchKernelGGL(scores_stream_kernel<false>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,
-                           rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,
-                           kv.max_pages, scores, score_stride);
+        QSA_SCAN(false, false);
+#undef QSA_SCAN
     return hipGetLastError();
 }
 
@@ -170,9 +180,14 @@ hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* score
                                hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
     dim3 grid((rows.R + 63) / 64, kv.Hkv, (score_stride + kTiledChunk - 1) / kTiledChunk);
-    hipLaunchKernelGGL(scores_tiled_kernel, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq, rows.q_pos,
-                       rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,
-                       kv.max_pages, scores, score_stride);
+    if (kv.ckey_bf16)
+        hipLaunchKernelGGL(scores_tiled_kernel<true>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,
+                           rows.q_pos, rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv,
+                           kv.lg_ps, kv.max_pages, scores, score_stride);
+    else
+        hipLaunchKernelGGL(scores_tiled_kernel<false>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,
+                           rows.q_pos, rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv,
+                           kv.lg_ps, kv.max_pages, scores, score_stride);
     return hipGetLastError();
 }
 

@@ -58,6 +58,8 @@ extern "C" {
 #define QSA_MAX_GROUP 16            /* query heads per KV head */
 #define QSA_MAX_SPLITS 64
 #define QSA_MAX_SEQ_LEN (1 << 20)   /* tokens per sequence */
+#define QSA_CKEY_FP32 0             /* block keys stored as fp32 */
+#define QSA_CKEY_BF16 1             /* block keys stored as bf16 (rounded fp32 means) */
 
 /*
  * Paged KV cache.  Page p of the pool holds, for every KV head, page_size
@@ -66,7 +68,12 @@ extern "C" {
  *   ckey   fp32  [num_pages][Hkv][page_size / 4][256]   block keys, paged by
  *                the same block table, so a page's keys and block keys never
  *                diverge (the DCP page keeps selector and main cache in one
- *                cache group for that reason).
+ *                cache group for that reason).  With ckey_dtype
+ *                QSA_CKEY_BF16 the same layout holds bf16 block keys: each is
+ *                the fp32 mean below rounded to the nearest bf16, ties to even
+ *                (half the bytes of the dominant decode stream; the page on
+ *                batch-sharded sampling, section on the surrounding patch
+ *                cluster, records smaller cache formats for this path).
  *   block_table int32 [batch][max_pages_per_seq]: token i of sequence s lives
  *                in page block_table[s][i / page_size], slot i % page_size.
  *   seq_lens    int32 [batch]: L_s, 0 <= L_s <= max_seq_len.
@@ -77,7 +84,7 @@ extern "C" {
 typedef struct qsa_kv {
     const void* k;
     const void* v;
-    float* ckey;
+    void* ckey;              /* fp32 or bf16 block keys, by ckey_dtype */
     const int32_t* block_table;
     const int32_t* seq_lens;
     int32_t batch;
@@ -87,6 +94,7 @@ typedef struct qsa_kv {
     int32_t num_pages;
     int32_t max_pages_per_seq;
     int32_t max_seq_len;
+    int32_t ckey_dtype;      /* QSA_CKEY_FP32 (0) or QSA_CKEY_BF16 */
 } qsa_kv_t;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -100,7 +108,8 @@ QSA_API const char* qsa_last_error(void);
  * with 4b < L_s and 4b + 3 >= first_token[s] (first_token NULL = 0), writes
  *   ckey[b] = fp32 mean of the block's n = min(4, L_s - 4b) keys,
  * computed exactly as ((k0 + k1) + (k2 + k3)) * 0.25 for n = 4 and as the
- * left-to-right sum divided by n (correctly rounded) for n < 4.  The pages
+ * left-to-right sum divided by n (correctly rounded) for n < 4 (bf16 block
+ * keys: that mean rounded to nearest, ties to even).  The pages
  * say only that keys are compressed into 4-token microblocks; this pooling is
  * the stated reading.  Idempotent: a page shared by two sequences gets the
  * same values from both.  Decode calls it with first_token = L_s - 1 to

@@ -75,10 +75,15 @@ class Dev:
 
     # ------------------------------------------------------------ views
     def ckey_logical(self, i: int) -> np.ndarray:
-        """Block keys of sequence i as [Hkv][nb][256] float32, gathered from the pool."""
+        """Block keys of sequence i as [Hkv][nb][256] float32 (bf16 keys widened), gathered
+        from the pool."""
         c = self.case
         nb = c.nb(i)
-        pool = self.t["ckey"].cpu().numpy()
+        t = self.t["ckey"]
+        if t.dtype == torch.bfloat16:  # widened to float32 (exact)
+            pool = synth.bf16_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+        else:
+            pool = t.cpu().numpy()
         b = np.arange(nb)
         pages = c.block_table[i][(4 * b) // c.page_size]
         slots = ((4 * b) % c.page_size) // 4
