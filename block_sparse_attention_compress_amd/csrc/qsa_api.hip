@@ -101,8 +101,10 @@ int check_q(const void* q, int64_t q_row_stride, int Hq) {
 }
 
 int auto_splits(int64_t units, int k) {
-    // aim at ~512 workgroups (2 resident per CU) while keeping >= 16 blocks per split
-    int64_t s = (512 + units - 1) / (units > 0 ? units : 1);
+    // aim at ~256 workgroups (one per CU) while keeping >= 16 blocks per split: a
+    // split sweep over 2-16 put the best step there for 2, 16 and 64 (row, KV head)
+    // units (64 units: S = 4 beat S = 8 by 3 %)
+    int64_t s = (256 + units - 1) / (units > 0 ? units : 1);
     const int64_t cap = k / 16 > 1 ? k / 16 : 1;
     if (s > cap) s = cap;
     if (s > 16) s = 16;
