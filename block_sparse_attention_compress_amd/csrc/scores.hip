@@ -51,10 +51,16 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
 // (c = lane & 15, kq = lane >> 4) holds, at k-step m, qsum[row c][64 kq + m] (A
 // operand) and ckey[block c][64 kq + m] (B operand): the same dim for A and B, so
 // the 64 steps of the 16x16x4 matrix-core op cover all 256 dims.  Output element
-// i of the lane is row 4 kq + i, block c of the tile.  The next 16-block tile's
-// keys are loaded while the current tile is multiplied.  Rows of one wave that
-// belong to different sequences are scored in separate passes.
+// i of the lane is row 4 kq + i, block c of the tile.
+//
+// When the workgroup's 64 rows belong to one sequence (the usual extend chunk),
+// its 4 waves share each 16-block tile of keys: the 256 threads load it together
+// (4 float4 each), it is staged in LDS (fp32, rows padded against bank
+// conflicts), and two tiles are in flight while one is multiplied.  Otherwise
+// each wave streams its own tiles, and rows of one wave that belong to different
+// sequences are scored in separate passes.
 constexpr int kTiledChunk = 512;
+constexpr int kTRow = kHeadDim + 4;  // padded key row of an LDS tile (floats)
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void scores_tiled_kernel(
@@ -62,20 +68,51 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
     const int32_t* __restrict__ q_pos, int R, int g, const void* __restrict__ ckey,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages,
     float* __restrict__ scores, int score_stride) {
+    __shared__ float ktile[2][16 * kTRow];
+    __shared__ int w_smin[4], w_smax[4], w_nend[4];
+    typedef typename KeyRaw<BF16>::type Raw;
+    const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
     const int h = blockIdx.y;
     const int bc0 = blockIdx.z * kTiledChunk;  // this workgroup's first block
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int wave = wave_id();
     const int r0 = blockIdx.x * 64 + wave * 16;
-    if (r0 >= R) return;
     const int c = lane & 15, kq = lane >> 4;
     const int row = r0 + c;
     const bool valid = row < R;
     const int seq_r = valid ? q_seq[row] : -1;
     const int t_r = valid ? q_pos[row] : -1;
     // rows whose eligible blocks all lie before this chunk take no part
-    const bool live = valid && t_r >= 0 && min(t_r / 4 + 1, score_stride) > bc0;
-    if (!__ballot(live)) return;
+    const int ne_row = valid && t_r >= 0 ? min(t_r / 4 + 1, score_stride) : 0;
+    const bool live = ne_row > bc0;
+    const int lg_bpp = lg_ps - 2;
+
+    // ---- one sequence for the whole workgroup?  (decided before any wave leaves)
+    {
+        int smin = live ? seq_r : 0x7fffffff, smax = live ? seq_r : -1;
+        int nend = live ? min(ne_row, bc0 + kTiledChunk) : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            smin = min(smin, __shfl_xor(smin, o));
+            smax = max(smax, __shfl_xor(smax, o));
+            nend = max(nend, __shfl_xor(nend, o));
+        }
+        if (lane == 0) {
+            w_smin[wave] = smin;
+            w_smax[wave] = smax;
+            w_nend[wave] = nend;
+        }
+    }
+    __syncthreads();
+    int smin = w_smin[0], smax = w_smax[0], wg_end = w_nend[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+        smin = min(smin, w_smin[w]);
+        smax = max(smax, w_smax[w]);
+        wg_end = max(wg_end, w_nend[w]);
+    }
+    if (smax < 0) return;  // no live row in the workgroup (uniform)
 
     float a[64];
 #pragma unroll
@@ -101,7 +138,79 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
             }
         }
     }
-    const int lg_bpp = lg_ps - 2;
+
+    if (smin == smax) {
+        // ---- shared tiles through LDS; every wave stays to the end (barriers)
+        const int s = smin;
+        const int nb_seq = (seq_lens[s] + 3) >> 2;
+        const int ne_c = live ? ne_row : 0;
+        int ne_out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ne_out[i] = __shfl(ne_c, 4 * kq + i);
+        const int wave_end = min(wave_max_int(ne_c), bc0 + kTiledChunk);
+        const int ntiles = (wg_end - bc0 + 15) / 16;
+        // this thread's share of a tile: block bl, float4 slots f0 + 16 j of its key
+        const int bl = tid >> 4, f0 = tid & 15;
+        auto load = [&](int t, Raw* gr) {
+            const int b = bc0 + 16 * t + bl;
+            if (b < nb_seq) {
+                const int64_t page = block_table[(int64_t)s * max_pages + (b >> lg_bpp)];
+                const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
+                const Raw* src = keys + brow * (kHeadDim / 4) + f0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) gr[j] = src[16 * j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) gr[j] = Raw{};
+            }
+        };
+        auto stage = [&](int slot, const Raw* gr) {
+            float* dst = ktile[slot] + bl * kTRow + 4 * f0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<float4*>(dst + 64 * j) = key4(gr[j]);
+        };
+        auto compute = [&](int t, int slot) {
+            const int bt0 = bc0 + 16 * t;
+            if (bt0 >= wave_end) return;  // this wave's rows are done (uniform per wave)
+            const float* src = ktile[slot] + c * kTRow + 64 * kq;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float4 kv = *reinterpret_cast<const float4*>(src + 4 * i);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 0], kv.x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 1], kv.y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 2], kv.z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 3], kv.w, acc, 0, 0, 0);
+            }
+            const int b = bt0 + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (b < ne_out[i]) scores[((int64_t)(r0 + 4 * kq + i) * Hkv + h) * score_stride + b] = acc[i];
+        };
+        // two register sets (named, so nothing is indexed across iterations) and two
+        // LDS slots: tile t is multiplied from slot t % 2 while tiles t + 1 and t + 2
+        // are in flight
+        Raw g0[4], g1[4];
+        load(0, g0);
+        if (ntiles > 1) load(1, g1);
+        stage(0, g0);
+        __syncthreads();
+        for (int t = 0; t < ntiles; t += 2) {
+            if (t + 2 < ntiles) load(t + 2, g0);
+            compute(t, 0);
+            if (t + 1 < ntiles) stage(1, g1);
+            __syncthreads();
+            if (t + 1 >= ntiles) break;
+            if (t + 3 < ntiles) load(t + 3, g1);
+            compute(t + 1, 1);
+            if (t + 2 < ntiles) stage(0, g0);
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---- rows of several sequences: each wave streams its own tiles
+    if (r0 >= R || !__ballot(live)) return;
     uint64_t pending = __ballot(live && kq == 0) & 0xffffull;
     while (pending) {
         const int first = __builtin_ctzll(pending);
@@ -109,14 +218,12 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
         const uint64_t active = __ballot(kq == 0 && live && seq_r == s) & 0xffffull;
         pending &= ~active;
         const int nb_seq = (seq_lens[s] + 3) >> 2;
-        const int ne_c = ((active >> c) & 1) ? min(t_r / 4 + 1, score_stride) : 0;
+        const int ne_c = ((active >> c) & 1) ? ne_row : 0;
         const int n_end = min(wave_max_int(ne_c), bc0 + kTiledChunk);
         int ne_out[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ne_out[i] = __shfl(ne_c, 4 * kq + i);
         // block keys of the tile at bt0 into v, raw (zeros past the sequence)
-        typedef typename KeyRaw<BF16>::type Raw;
-        const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
         auto load_tile = [&](int bt0, Raw* v) {
             const int b = bt0 + c;
             if (b < nb_seq) {
