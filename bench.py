@@ -230,7 +230,7 @@ def main():
     compress_full_ms = e0.elapsed_time(e1)
 
     splits = (0 if case.splits == 1 else case.splits) if args.splits is None else args.splits
-    ws = buf.workspace
+    ws, tw = buf.workspace, buf.topk_workspace
 
     def step(ev=None):
         # the same calls as pipeline.decode_step, with events between the launches
@@ -242,7 +242,8 @@ def main():
         qsa.qsa_block_scores(kv, q, q.stride(0), None, None, case.B, case.Hq, buf.scores, stride)
         if ev is not None:
             ev[2].record()
-        qsa.qsa_topk_blocks(buf.scores, stride, q_pos, case.B, case.Hkv, case.topk, buf.sel_idx, buf.sel_cnt)
+        qsa.qsa_topk_blocks_ws(buf.scores, stride, q_pos, case.B, case.Hkv, case.topk, buf.sel_idx, buf.sel_cnt,
+                               workspace=tw, workspace_bytes=0 if tw is None else tw.numel())
         if ev is not None:
             ev[3].record()
         qsa.qsa_sparse_attn_decode(kv, q, q.stride(0), case.Hq, buf.sel_idx, buf.sel_cnt, case.topk, case.scale,

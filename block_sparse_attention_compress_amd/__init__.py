@@ -6,7 +6,7 @@ current HIP stream; every step runs in the library's HIP kernels.  The C
 declarations, with the meaning, layout and error behaviour of every argument,
 are in ``include/qsa.h``.  The functions keep the C names:
 
-    qsa_compress_keys, qsa_block_scores, qsa_topk_blocks,
+    qsa_compress_keys, qsa_block_scores, qsa_topk_blocks, qsa_topk_blocks_ws,
     qsa_sparse_attn_decode, qsa_sparse_attn_extend, qsa_merge_lse,
     qsa_decode_fused (scores + top-k + attention + merge in one launch)
 
@@ -38,7 +38,8 @@ CKEY_BF16 = 1
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks",
            "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse",
-           "qsa_decode_fused", "qsa_decode_fused_workspace_bytes")
+           "qsa_decode_fused", "qsa_decode_fused_workspace_bytes", "qsa_topk_blocks_ws",
+           "qsa_topk_workspace_bytes")
 
 
 class QsaError(RuntimeError):
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_compress_keys.argtypes = [kvp, vp, i32, vp]
         L.qsa_block_scores.argtypes = [kvp, vp, i64, vp, vp, i32, i32, vp, i32, vp]
         L.qsa_topk_blocks.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp]
+        L.qsa_topk_blocks_ws.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.qsa_topk_workspace_bytes.argtypes, L.qsa_topk_workspace_bytes.restype = [i32, i32, i32, i32], sz
         L.qsa_sparse_attn_decode.argtypes = [kvp, vp, i64, i32, vp, vp, i32, f32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
         L.qsa_decode_workspace_bytes.argtypes, L.qsa_decode_workspace_bytes.restype = [i32, i32, i32], sz
         L.qsa_sparse_attn_extend.argtypes = [kvp, vp, i64, vp, vp, i32, i32, vp, vp, i32, f32, vp, i64, vp, vp]
@@ -90,7 +93,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_decode_fused.argtypes = [kvp, vp, i64, i32, i32, f32, i32, vp, vp, vp, i64, vp, vp, sz, vp]
         L.qsa_decode_fused_workspace_bytes.argtypes = [kvp, i32, i32, i32]
         L.qsa_decode_fused_workspace_bytes.restype = sz
-        for f in ("qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks", "qsa_sparse_attn_decode",
+        for f in ("qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks", "qsa_topk_blocks_ws",
+                  "qsa_sparse_attn_decode",
                   "qsa_sparse_attn_extend", "qsa_merge_lse", "qsa_decode_fused"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -170,6 +174,16 @@ def qsa_topk_blocks(scores, score_stride: int, q_pos, R: int, Hkv: int, k: int, 
                     stream=None) -> None:
     _check(lib().qsa_topk_blocks(_ptr(scores), score_stride, _ptr(q_pos), R, Hkv, k, _ptr(sel_idx), _ptr(sel_cnt),
                                  _stream(stream)))
+
+
+def qsa_topk_workspace_bytes(R: int, Hkv: int, k: int, score_stride: int) -> int:
+    return int(lib().qsa_topk_workspace_bytes(R, Hkv, k, score_stride))
+
+
+def qsa_topk_blocks_ws(scores, score_stride: int, q_pos, R: int, Hkv: int, k: int, sel_idx, sel_cnt,
+                       workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    _check(lib().qsa_topk_blocks_ws(_ptr(scores), score_stride, _ptr(q_pos), R, Hkv, k, _ptr(sel_idx),
+                                    _ptr(sel_cnt), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def qsa_decode_workspace_bytes(batch: int, Hq: int, num_splits: int) -> int:

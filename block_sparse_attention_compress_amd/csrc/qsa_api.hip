@@ -155,8 +155,8 @@ int qsa_block_scores(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, co
     return hip_status(e, "qsa_block_scores");
 }
 
-int qsa_topk_blocks(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R, int32_t Hkv,
-                    int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
+static int check_topk(const float* scores, int32_t score_stride, int32_t R, int32_t Hkv, int32_t k,
+                      const int32_t* sel_idx, const int32_t* sel_cnt) {
     if (!scores) return fail(QSA_ERR_INVALID_ARG, "scores is NULL");
     if (score_stride < 1 || score_stride > QSA_MAX_SEQ_LEN / QSA_MICROBLOCK)
         return fail(QSA_ERR_INVALID_ARG, "score_stride %d out of [1, %d]", score_stride,
@@ -165,9 +165,38 @@ int qsa_topk_blocks(const float* scores, int32_t score_stride, const int32_t* q_
     if ((int64_t)R * Hkv > 0x7fffffff) return fail(QSA_ERR_UNSUPPORTED, "R * Hkv exceeds 2^31 - 1");
     if (k < 0 || k > QSA_MAX_TOPK) return fail(QSA_ERR_INVALID_ARG, "k %d out of [0, %d]", k, QSA_MAX_TOPK);
     if (!sel_cnt || (k > 0 && !sel_idx)) return fail(QSA_ERR_INVALID_ARG, "sel_idx / sel_cnt is NULL");
+    return QSA_OK;
+}
+
+int qsa_topk_blocks(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R, int32_t Hkv,
+                    int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
+    if (int rc = check_topk(scores, score_stride, R, Hkv, k, sel_idx, sel_cnt)) return rc;
     return hip_status(qsa::launch_topk(scores, score_stride, q_pos, R, Hkv, k, sel_idx, sel_cnt,
                                        static_cast<hipStream_t>(stream)),
                       "qsa_topk_blocks");
+}
+
+size_t qsa_topk_workspace_bytes(int32_t R, int32_t Hkv, int32_t k, int32_t score_stride) {
+    if (R <= 0 || Hkv <= 0 || k < 0 || k > QSA_MAX_TOPK || score_stride < 1 ||
+        score_stride > QSA_MAX_SEQ_LEN / QSA_MICROBLOCK || (int64_t)R * Hkv > 0x7fffffff)
+        return 0;
+    return qsa::topk_workspace_bytes(R, Hkv, k, score_stride);
+}
+
+int qsa_topk_blocks_ws(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R, int32_t Hkv,
+                       int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (int rc = check_topk(scores, score_stride, R, Hkv, k, sel_idx, sel_cnt)) return rc;
+    const size_t need = qsa::topk_workspace_bytes(R, Hkv, k, score_stride);
+    if (need > 0) {
+        if (!workspace) return fail(QSA_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(QSA_ERR_INVALID_ARG, "workspace_bytes %zu < %zu", workspace_bytes, need);
+        if (!aligned(workspace, 16)) return fail(QSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
+    return hip_status(qsa::launch_topk_split(scores, score_stride, q_pos, R, Hkv, k, sel_idx, sel_cnt, workspace,
+                                             static_cast<hipStream_t>(stream)),
+                      "qsa_topk_blocks_ws");
 }
 
 size_t qsa_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t num_splits) {

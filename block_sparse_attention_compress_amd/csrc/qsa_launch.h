@@ -36,6 +36,11 @@ hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* score
 
 hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,
                        int32_t* sel_idx, int32_t* sel_cnt, hipStream_t st);
+// two-stage select for long rows through a candidate workspace of
+// topk_workspace_bytes() bytes (0: one stage, same as launch_topk)
+size_t topk_workspace_bytes(int R, int Hkv, int k, int score_stride);
+hipError_t launch_topk_split(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,
+                             int32_t* sel_idx, int32_t* sel_cnt, void* workspace, hipStream_t st);
 
 struct AttnOut {
     uint16_t* out;            // bf16, final result (num_splits == 1 and part_out == NULL)

@@ -82,11 +82,20 @@ constexpr int kBins = 2048;
 
 // KPT scores per thread: the first KR in registers, the rest in LDS (a 65,536-block
 // row would not fit 1024 threads x 128 registers).
-template <int KPT, int KR>
+// Candidate workspace of the two-stage select for long rows: per (row, KV head),
+// nslices x k (value, block index) pairs, slice j's top k in ascending index order.
+struct SplitWs {
+    float* val;
+    int32_t* idx;
+    int slice;    // blocks per slice (a multiple of 1024, >= 4 QSA_MAX_TOPK)
+    int nslices;  // ceil(score_stride / slice)
+};
+
+template <int KPT, int KR, int MODE>
 __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __restrict__ scores, int score_stride,
                                                                const int32_t* __restrict__ q_pos, int Hkv, int k,
                                                                int32_t* __restrict__ sel_idx,
-                                                               int32_t* __restrict__ sel_cnt) {
+                                                               int32_t* __restrict__ sel_cnt, SplitWs ws) {
     __shared__ int hist[kBins];
     __shared__ float cand_val[kRegThreads];
     __shared__ int cand_idx[kRegThreads];
@@ -98,13 +107,57 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     __shared__ float vl[KL > 0 ? KL * kRegThreads : 1];
 
     const int unit = blockIdx.x;
-    const int n = eligible(q_pos, unit / Hkv, score_stride);
+    const int n_row = eligible(q_pos, unit / Hkv, score_stride);
     int32_t* out = sel_idx + (int64_t)unit * k;
-    if (topk_trivial(n, k, out, sel_cnt + unit)) return;
+    const float* s = scores + (int64_t)unit * score_stride;
+    int n = n_row, row_len = score_stride;
+    // MODE 1: slice blockIdx.y of the row.  A row that fits one slice is finished
+    // here (final output); a longer one leaves the slice's top k as candidates.
+    // MODE 2: the candidates of a row longer than one slice.
+    bool final_out = true;
+    int base = 0;  // block index of this slice's first score
+    float* cv = nullptr;
+    int32_t* ci = nullptr;
+    if (MODE == 1) {
+        base = blockIdx.y * ws.slice;
+        if (n_row > ws.slice) {
+            if (base >= n_row || k == 0) return;
+            final_out = false;
+            s += base;
+            n = min(ws.slice, n_row - base);
+            row_len = min(ws.slice, score_stride - base);
+            cv = ws.val + ((int64_t)unit * ws.nslices + blockIdx.y) * k;
+            ci = ws.idx + ((int64_t)unit * ws.nslices + blockIdx.y) * k;
+            if (n <= k) {  // a short last slice: all of it
+                for (int j = threadIdx.x; j < k; j += blockDim.x) {
+                    cv[j] = j < n ? s[j] + 0.0f : -INFINITY;
+                    ci[j] = j < n ? base + j : -1;
+                }
+                return;
+            }
+        } else if (blockIdx.y > 0) {
+            return;
+        }
+    } else if (MODE == 2) {
+        if (n_row <= ws.slice) return;
+        row_len = ws.nslices * k;
+        n = ((n_row + ws.slice - 1) / ws.slice) * k;  // slices holding eligible blocks
+        s = ws.val + (int64_t)unit * row_len;
+        ci = ws.idx + (int64_t)unit * row_len;
+    }
+    if (final_out && topk_trivial(n_row, k, out, sel_cnt + unit)) return;
+    // emit(j, i): the j-th selected (ascending) is local position i
+    auto emit = [&](int j, int i, float x) {
+        if (MODE == 2) out[j] = ci[i];
+        else if (MODE == 1 && !final_out) {
+            cv[j] = x;
+            ci[j] = base + i;
+        } else
+            out[j] = i;
+    };
 
     const int tid = threadIdx.x;
     const int i0 = tid * KPT;  // this thread's first block
-    const float* s = scores + (int64_t)unit * score_stride;
     // slots past n hold -inf (scores are finite): it is never selected, and
     // every test below stays a function of the value (no per-slot masks kept live)
     float v[KR];
@@ -113,9 +166,9 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
         if (e < KR) v[e < KR ? e : 0] = x;
         else vl[(e - KR) * kRegThreads + tid] = x;
     };
-    if (KPT >= 4 && (score_stride & 3) == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
+    if (KPT >= 4 && (row_len & 3) == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
         // float4 loads, clamped and unconditional, so all KPT / 4 are in flight at once
-        // (a whole float4 lies inside the row: n4 <= score_stride / 4)
+        // (a whole float4 lies inside the row: n4 <= row_len / 4)
         const float4* s4 = reinterpret_cast<const float4*>(s);
         const int n4 = (n + 3) / 4;
 #pragma unroll
@@ -138,9 +191,9 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
         mx = fmaxf(mx, V(e));
     }
     const float range = block_min_max(mn, mx, ftmp);
-    if (range == 0.f) {  // every score equal: the k lowest indices
-        for (int j = tid; j < k; j += kRegThreads) out[j] = j;
-        if (tid == 0) sel_cnt[unit] = k;
+    if (range == 0.f) {  // every score equal: the k lowest indices (positions are in index order)
+        for (int j = tid; j < k; j += kRegThreads) emit(j, j, mn);
+        if (tid == 0 && final_out) sel_cnt[unit] = k;
         return;
     }
     float scale = (float)kBins / range;
@@ -262,14 +315,14 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
         if (V(e) == -INFINITY) continue;
         const uint32_t key = order_key(V(e));
         if (key > T) {
-            out[gt + min(eq, need_eq)] = i0 + e;
+            emit(gt + min(eq, need_eq), i0 + e, V(e));
             ++gt;
         } else if (key == T) {
-            if (eq < need_eq) out[gt + eq] = i0 + e;
+            if (eq < need_eq) emit(gt + eq, i0 + e, V(e));
             ++eq;
         }
     }
-    if (tid == 0) sel_cnt[unit] = k;
+    if (tid == 0 && final_out) sel_cnt[unit] = k;
 }
 
 // --------------------------------------------------------------------- global
@@ -372,11 +425,20 @@ __global__ __launch_bounds__(kGlobThreads) void topk_global_kernel(const float* 
     if (tid == 0) sel_cnt[unit] = k;
 }
 
-template <int KPT, int KR>
-static void launch_reg(const float* scores, int score_stride, const int32_t* q_pos, int units, int Hkv, int k,
-                       int32_t* sel_idx, int32_t* sel_cnt, hipStream_t st) {
-    hipLaunchKernelGGL((topk_reg_kernel<KPT, KR>), dim3(units), dim3(kRegThreads), 0, st, scores, score_stride, q_pos, Hkv,
-                       k, sel_idx, sel_cnt);
+template <int MODE>
+static void launch_reg(int per, dim3 grid, const float* scores, int score_stride, const int32_t* q_pos, int Hkv, int k,
+                       int32_t* sel_idx, int32_t* sel_cnt, SplitWs ws, hipStream_t st) {
+#define QSA_TOPK_REG(KPT, KR)                                                                                  \
+    hipLaunchKernelGGL((topk_reg_kernel<KPT, KR, MODE>), grid, dim3(kRegThreads), 0, st, scores, score_stride, \
+                       q_pos, Hkv, k, sel_idx, sel_cnt, ws)
+    if (per <= 1) QSA_TOPK_REG(1, 1);
+    else if (per <= 2) QSA_TOPK_REG(2, 2);
+    else if (per <= 4) QSA_TOPK_REG(4, 4);
+    else if (per <= 8) QSA_TOPK_REG(8, 8);
+    else if (per <= 16) QSA_TOPK_REG(16, 16);
+    else if (per <= 32) QSA_TOPK_REG(32, 32);
+    else QSA_TOPK_REG(64, 32);
+#undef QSA_TOPK_REG
 }
 
 hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,
@@ -384,16 +446,47 @@ hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_p
     if (R == 0) return hipSuccess;
     const int units = R * Hkv;
     const int per = (score_stride + kRegThreads - 1) / kRegThreads;  // scores per thread
-    if (per <= 1) launch_reg<1, 1>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
-    else if (per <= 2) launch_reg<2, 2>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
-    else if (per <= 4) launch_reg<4, 4>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
-    else if (per <= 8) launch_reg<8, 8>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
-    else if (per <= 16) launch_reg<16, 16>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
-    else if (per <= 32) launch_reg<32, 32>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
-    else if (per <= 64) launch_reg<64, 32>(scores, score_stride, q_pos, units, Hkv, k, sel_idx, sel_cnt, st);
+    if (per <= 64)
+        launch_reg<0>(per, dim3(units), scores, score_stride, q_pos, Hkv, k, sel_idx, sel_cnt, SplitWs{}, st);
     else
         hipLaunchKernelGGL(topk_global_kernel, dim3(units), dim3(kGlobThreads), 0, st, scores, score_stride, q_pos,
                            Hkv, k, sel_idx, sel_cnt);
+    return hipGetLastError();
+}
+
+// Rows longer than kSplitMin blocks are selected in two stages: every slice of
+// kSlice blocks keeps its own top k (one workgroup per slice, so a row spreads
+// over many CUs), then one workgroup per row selects the top k of the slices'
+// candidates.  A block in the row's top k is in its slice's top k (fewer than k
+// blocks of the slice precede it in the order), and the candidates sit in block
+// order, so the second stage, breaking ties by position, gives exactly the
+// one-stage result.
+constexpr int kSlice = 8192;
+constexpr int kSplitMin = 16384;
+
+static bool split_applies(int score_stride, int k) { return k >= 1 && score_stride > kSplitMin; }
+
+size_t topk_workspace_bytes(int R, int Hkv, int k, int score_stride) {
+    if (R <= 0 || Hkv <= 0 || !split_applies(score_stride, k)) return 0;
+    const int64_t per_unit = (int64_t)((score_stride + kSlice - 1) / kSlice) * k;
+    const size_t half = ((size_t)R * Hkv * per_unit * 4 + 255) & ~(size_t)255;
+    return 2 * half;
+}
+
+hipError_t launch_topk_split(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,
+                             int32_t* sel_idx, int32_t* sel_cnt, void* workspace, hipStream_t st) {
+    if (!split_applies(score_stride, k))
+        return launch_topk(scores, score_stride, q_pos, R, Hkv, k, sel_idx, sel_cnt, st);
+    if (R == 0) return hipSuccess;
+    const int units = R * Hkv;
+    const int nslices = (score_stride + kSlice - 1) / kSlice;
+    const size_t half = topk_workspace_bytes(R, Hkv, k, score_stride) / 2;
+    SplitWs ws{static_cast<float*>(workspace),
+               reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + half), kSlice, nslices};
+    launch_reg<1>(kSlice / kRegThreads, dim3(units, nslices), scores, score_stride, q_pos, Hkv, k, sel_idx, sel_cnt,
+                  ws, st);
+    const int per2 = (nslices * k + kRegThreads - 1) / kRegThreads;  // <= 32 * 2048 / 1024
+    launch_reg<2>(per2, dim3(units), scores, score_stride, q_pos, Hkv, k, sel_idx, sel_cnt, ws, st);
     return hipGetLastError();
 }
 

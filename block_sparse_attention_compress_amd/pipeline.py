@@ -13,7 +13,7 @@ import torch
 
 from . import (HEAD_DIM, KVCache, qsa_block_scores, qsa_compress_keys, qsa_decode_fused,
                qsa_decode_fused_workspace_bytes, qsa_decode_workspace_bytes, qsa_sparse_attn_decode,
-               qsa_sparse_attn_extend, qsa_topk_blocks)
+               qsa_sparse_attn_extend, qsa_topk_blocks, qsa_topk_blocks_ws, qsa_topk_workspace_bytes)
 
 
 @dataclass
@@ -26,6 +26,7 @@ class DecodeBuffers:
     out: torch.Tensor         # bf16 [B][Hq][256]
     lse: torch.Tensor         # fp32 [B][Hq]
     workspace: Optional[torch.Tensor]
+    topk_workspace: Optional[torch.Tensor]  # candidates of the two-stage select (long rows)
     score_stride: int
     k: int
 
@@ -33,6 +34,7 @@ class DecodeBuffers:
     def allocate(B: int, Hq: int, Hkv: int, score_stride: int, k: int, num_splits: int = 0,
                  device="cuda") -> "DecodeBuffers":
         ws_bytes = qsa_decode_workspace_bytes(B, Hq, num_splits)
+        tk_bytes = qsa_topk_workspace_bytes(B, Hkv, k, score_stride)
         return DecodeBuffers(
             scores=torch.empty((B, Hkv, score_stride), dtype=torch.float32, device=device),
             sel_idx=torch.empty((B, Hkv, max(k, 1)), dtype=torch.int32, device=device),
@@ -40,6 +42,7 @@ class DecodeBuffers:
             out=torch.empty((B, Hq, HEAD_DIM), dtype=torch.bfloat16, device=device),
             lse=torch.empty((B, Hq), dtype=torch.float32, device=device),
             workspace=torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None,
+            topk_workspace=torch.empty(tk_bytes, dtype=torch.uint8, device=device) if tk_bytes else None,
             score_stride=score_stride, k=k)
 
 
@@ -53,7 +56,9 @@ def decode_step(kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: DecodeBu
     if refresh_keys:
         qsa_compress_keys(kv, q_pos, 1, stream=stream)
     qsa_block_scores(kv, q, q.stride(0), None, None, B, Hq, buf.scores, buf.score_stride, stream=stream)
-    qsa_topk_blocks(buf.scores, buf.score_stride, q_pos, B, Hkv, buf.k, buf.sel_idx, buf.sel_cnt, stream=stream)
+    tw = buf.topk_workspace
+    qsa_topk_blocks_ws(buf.scores, buf.score_stride, q_pos, B, Hkv, buf.k, buf.sel_idx, buf.sel_cnt, workspace=tw,
+                       workspace_bytes=0 if tw is None else tw.numel(), stream=stream)
     ws = buf.workspace
     qsa_sparse_attn_decode(kv, q, q.stride(0), Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale, num_splits, buf.out,
                            buf.out.stride(0), buf.lse, workspace=ws, workspace_bytes=0 if ws is None else ws.numel(),

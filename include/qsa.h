@@ -150,6 +150,26 @@ QSA_API int qsa_topk_blocks(const float* scores, int32_t score_stride, const int
                     int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* stream);
 
 /*
+ * a3, long rows -- the same selection as qsa_topk_blocks, bit for bit, for
+ * rows longer than 16,384 blocks computed in two launches: every 8,192-block
+ * slice of a row keeps its own top k (so one row spreads over many compute
+ * units), then the top k of those candidates is taken.  The candidates live in
+ * `workspace` (device memory, 16-byte aligned, caller-owned, contents on entry
+ * ignored and on return unspecified), which must hold
+ * qsa_topk_workspace_bytes(R, Hkv, k, score_stride) bytes; when that is 0 the
+ * call is qsa_topk_blocks and workspace may be NULL.  Arguments and errors as
+ * qsa_topk_blocks, plus QSA_ERR_INVALID_ARG for a missing, short or misaligned
+ * workspace.  Calls sharing one workspace must be ordered on one stream.
+ */
+QSA_API int qsa_topk_blocks_ws(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R,
+                               int32_t Hkv, int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace bytes qsa_topk_blocks_ws needs (0 for rows that are selected in
+ * one stage, for k == 0, and for arguments qsa_topk_blocks would reject). */
+QSA_API size_t qsa_topk_workspace_bytes(int32_t R, int32_t Hkv, int32_t k, int32_t score_stride);
+
+/*
  * a4 -- sparse attention, decode (one row per sequence at t = L_s - 1).
  * sel_idx / sel_cnt as written by qsa_topk_blocks ([batch][Hkv][k], ascending,
  * every block eligible).  For query head j of KV head h the token set is

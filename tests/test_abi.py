@@ -108,6 +108,29 @@ def test_topk_rejects():
     assert status(L, P, 100, None, 2, 0, 16, P, P, None) == qsa.QSA_ERR_INVALID_ARG
 
 
+def test_topk_ws_rejects_and_sizes():
+    """The two-stage select: same argument checks as the one-stage call, plus the
+    candidate workspace (two arrays of ceil(stride / 8192) * k entries per row and
+    KV head, each rounded up to 256 bytes); rows of up to 16,384 blocks need none."""
+    W = qsa.qsa_topk_workspace_bytes
+    assert W(4, 2, 512, 16384) == 0
+    assert W(4, 2, 0, 65536) == 0
+    assert W(0, 2, 512, 65536) == 0
+    assert W(4, 2, 2049, 65536) == 0 and W(4, 2, 512, (1 << 18) + 1) == 0
+    assert W(1, 1, 512, 16385) == 2 * 6144
+    assert W(8, 2, 512, 65536) == 2 * 16 * 8 * 512 * 4
+    assert W(3, 1, 17, 20001) == 2 * ((3 * 3 * 17 * 4 + 255) // 256 * 256)
+    L = "qsa_topk_blocks_ws"
+    need = W(2, 2, 512, 65536)
+    assert status(L, P, 65536, None, 2, 2, 512, P, P, None, need, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 65536, None, 2, 2, 512, P, P, P, need - 1, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 65536, None, 2, 2, 512, P, P, P + 4, need, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, None, 65536, None, 2, 2, 512, P, P, P, need, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 65536, None, 2, 2, 2049, P, P, P, need, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 65536, None, 2, 0, 512, P, P, P, need, None) == qsa.QSA_ERR_INVALID_ARG
+    assert status(L, P, 65536, None, 2, 2, 512, None, P, P, need, None) == qsa.QSA_ERR_INVALID_ARG
+
+
 def test_decode_rejects():
     d = kv()
     f = qsa.lib().qsa_sparse_attn_decode
