@@ -34,7 +34,8 @@ if ROOT not in sys.path:
 METRIC = "QSA decode queries/s and achieved HBM GB/s (% of MI355X peak) at 64K ctx"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scores_stream_kernel_C2_traffic.json")
-SCORES_SRC = [os.path.join(ROOT, "block_sparse_attention_compress_amd", "csrc", f) for f in ("scores.hip", "scan_body.h")]
+SCORES_SRC = [os.path.join(ROOT, "block_sparse_attention_compress_amd", "csrc", f)
+              for f in ("scores.hip", "scan_body.h", "qsa_device.h")]
 
 
 def log(msg: str):
@@ -104,19 +105,22 @@ def copy_calibration():
 
 
 def decode_bytes(case, sel, cnt, page_size):
-    """Algorithmic HBM bytes of one decode step, and of its block-score launch.
+    """Algorithmic HBM bytes of one decode step, and of its refresh-and-score launch.
 
     step: per (sequence, KV head) the block-key scan (nb * 1 KiB for fp32 keys,
-    nb * 512 B for bf16 keys) and the
-    bf16 K and V rows of the selected tokens (512 B each), plus q and out rows
-    (bf16), lse (fp32), the block table and the lengths.
-    scores launch: the block-key scan, the q rows, the score writes (4 B per block)
-    and the block table."""
+    nb * 512 B for bf16 keys), the rebuilt newest block key (its 1..4 bf16 K rows
+    read, one block key written) and the bf16 K and V rows of the selected tokens
+    (512 B each), plus q and out rows (bf16), lse (fp32), the block table and the
+    lengths.
+    refresh-and-score launch: the block-key scan, the rebuilt key, the q rows,
+    the score writes (4 B per block) and the block table."""
     import numpy as np
 
     B, Hkv, Hq = case.B, case.Hkv, case.Hq
     nb = np.array([case.nb(i) for i in range(B)], dtype=np.int64)
-    ckey = int(nb.sum()) * Hkv * 256 * (2 if case.ckey_dtype == "bf16" else 4)
+    key_bytes = 256 * (2 if case.ckey_dtype == "bf16" else 4)
+    ckey = int(nb.sum()) * Hkv * key_bytes
+    refresh = sum((int(L) - 4 * ((int(L) - 1) // 4)) * 512 + key_bytes for L in case.lens if L > 0) * Hkv
     tokens = 0
     for i in range(B):
         L = int(case.lens[i])
@@ -127,8 +131,8 @@ def decode_bytes(case, sel, cnt, page_size):
     kv_bytes = tokens * 256 * 2 * 2
     qo = B * Hq * 256 * 2 * 2 + B * Hq * 4
     table = int(sum((int(L) + page_size - 1) // page_size for L in case.lens)) * 4 + B * 4
-    step = ckey + kv_bytes + qo + table
-    scores = ckey + B * Hq * 256 * 2 + int(nb.sum()) * Hkv * 4 + table
+    step = ckey + refresh + kv_bytes + qo + table
+    scores = ckey + refresh + B * Hq * 256 * 2 + int(nb.sum()) * Hkv * 4 + table
     return step, scores, tokens
 
 
@@ -236,32 +240,29 @@ def main():
         # the same calls as pipeline.decode_step, with events between the launches
         if ev is not None:
             ev[0].record()
-        qsa.qsa_compress_keys(kv, q_pos, 1)
+        qsa.qsa_decode_scores_refresh(kv, q, q.stride(0), case.Hq, buf.scores, stride)
         if ev is not None:
             ev[1].record()
-        qsa.qsa_block_scores(kv, q, q.stride(0), None, None, case.B, case.Hq, buf.scores, stride)
-        if ev is not None:
-            ev[2].record()
         qsa.qsa_topk_blocks_ws(buf.scores, stride, q_pos, case.B, case.Hkv, case.topk, buf.sel_idx, buf.sel_cnt,
                                workspace=tw, workspace_bytes=0 if tw is None else tw.numel())
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
         qsa.qsa_sparse_attn_decode(kv, q, q.stride(0), case.Hq, buf.sel_idx, buf.sel_cnt, case.topk, case.scale,
                                    splits, buf.out, buf.out.stride(0), buf.lse, workspace=ws,
                                    workspace_bytes=0 if ws is None else ws.numel())
         if ev is not None:
-            ev[4].record()
+            ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     # (1) eager steps with HIP events between the launches: per-kernel times
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
-    parts = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in events])  # ms
+    parts = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(3)] for ev in events])  # ms
     part_ms = parts.mean(axis=0)
     # (2) eager steps, nothing between the launches
     torch.cuda.synchronize()
@@ -307,7 +308,7 @@ def main():
     sel = buf.sel_idx.cpu().numpy()
     cnt = buf.sel_cnt.cpu().numpy()
     step_bytes, scores_bytes, tokens = decode_bytes(case, sel, cnt, case.page_size)
-    scores_s = part_ms[1] / 1e3
+    scores_s = part_ms[0] / 1e3
     achieved = scores_bytes / scores_s / 1e9
 
     traffic = None
@@ -335,12 +336,12 @@ def main():
                    "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "scores_stream_kernel (block-score scan)",
-                     "algorithmic_bytes_per_launch": scores_bytes, "avg_launch_ms": round(part_ms[1], 5)},
+                     "kernel": "scores_stream_kernel (newest block key rebuilt + block-score scan)",
+                     "algorithmic_bytes_per_launch": scores_bytes, "avg_launch_ms": round(part_ms[0], 5)},
         "step": {"algorithmic_bytes": step_bytes, "algorithmic_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
                  "selected_tokens": tokens,
-                 "event_ms": {"compress_refresh": round(part_ms[0], 5), "block_scores": round(part_ms[1], 5),
-                              "topk": round(part_ms[2], 5), "attention_and_merge": round(part_ms[3], 5)},
+                 "event_ms": {"refresh_and_scores": round(part_ms[0], 5), "topk": round(part_ms[1], 5),
+                              "attention_and_merge": round(part_ms[2], 5)},
                  "execution": mode, "eager_ms_per_step": round(eager_ms, 4), "fused_single_launch": fused,
                  "full_block_key_build_ms": round(compress_full_ms, 4)},
     }

@@ -6,7 +6,7 @@ current HIP stream; every step runs in the library's HIP kernels.  The C
 declarations, with the meaning, layout and error behaviour of every argument,
 are in ``include/qsa.h``.  The functions keep the C names:
 
-    qsa_compress_keys, qsa_block_scores, qsa_topk_blocks, qsa_topk_blocks_ws,
+    qsa_compress_keys, qsa_block_scores, qsa_decode_scores_refresh, qsa_topk_blocks, qsa_topk_blocks_ws,
     qsa_sparse_attn_decode, qsa_sparse_attn_extend, qsa_merge_lse,
     qsa_decode_fused (scores + top-k + attention + merge in one launch)
 
@@ -39,7 +39,7 @@ CKEY_BF16 = 1
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks",
            "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse",
            "qsa_decode_fused", "qsa_decode_fused_workspace_bytes", "qsa_topk_blocks_ws",
-           "qsa_topk_workspace_bytes")
+           "qsa_topk_workspace_bytes", "qsa_decode_scores_refresh")
 
 
 class QsaError(RuntimeError):
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_last_error.argtypes, L.qsa_last_error.restype = [], ctypes.c_char_p
         L.qsa_compress_keys.argtypes = [kvp, vp, i32, vp]
         L.qsa_block_scores.argtypes = [kvp, vp, i64, vp, vp, i32, i32, vp, i32, vp]
+        L.qsa_decode_scores_refresh.argtypes = [kvp, vp, i64, i32, vp, i32, vp]
         L.qsa_topk_blocks.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp]
         L.qsa_topk_blocks_ws.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.qsa_topk_workspace_bytes.argtypes, L.qsa_topk_workspace_bytes.restype = [i32, i32, i32, i32], sz
@@ -93,7 +94,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_decode_fused.argtypes = [kvp, vp, i64, i32, i32, f32, i32, vp, vp, vp, i64, vp, vp, sz, vp]
         L.qsa_decode_fused_workspace_bytes.argtypes = [kvp, i32, i32, i32]
         L.qsa_decode_fused_workspace_bytes.restype = sz
-        for f in ("qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks", "qsa_topk_blocks_ws",
+        for f in ("qsa_compress_keys", "qsa_block_scores", "qsa_decode_scores_refresh", "qsa_topk_blocks",
+                  "qsa_topk_blocks_ws",
                   "qsa_sparse_attn_decode",
                   "qsa_sparse_attn_extend", "qsa_merge_lse", "qsa_decode_fused"):
             getattr(L, f).restype = ctypes.c_int
@@ -168,6 +170,12 @@ def qsa_block_scores(kv, q, q_row_stride: int, q_seq, q_pos, R: int, Hq: int, sc
     d = _kv(kv)
     _check(lib().qsa_block_scores(ctypes.byref(d), _ptr(q), q_row_stride, _ptr(q_seq), _ptr(q_pos), R, Hq,
                                   _ptr(scores), score_stride, _stream(stream)))
+
+
+def qsa_decode_scores_refresh(kv, q, q_row_stride: int, Hq: int, scores, score_stride: int, stream=None) -> None:
+    d = _kv(kv)
+    _check(lib().qsa_decode_scores_refresh(ctypes.byref(d), _ptr(q), q_row_stride, Hq, _ptr(scores), score_stride,
+                                           _stream(stream)))
 
 
 def qsa_topk_blocks(scores, score_stride: int, q_pos, R: int, Hkv: int, k: int, sel_idx, sel_cnt,

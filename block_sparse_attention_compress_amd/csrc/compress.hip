@@ -65,19 +65,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restric
             const float k1 = half ? bf16_hi(w1) : bf16_lo(w1);
             const float k2 = half ? bf16_hi(w2) : bf16_lo(w2);
             const float k3 = half ? bf16_hi(w3) : bf16_lo(w3);
-            float v;
-            if (n == 4) {
-                const float s01 = k0 + k1;
-                const float s23 = k2 + k3;
-                v = (s01 + s23) * 0.25f;
-            } else if (n == 3) {
-                v = __fdiv_rn((k0 + k1) + k2, 3.0f);
-            } else if (n == 2) {
-                v = (k0 + k1) * 0.5f;  // exact halving == division by 2
-            } else {
-                v = k0;
-            }
-            r[2 * w + half] = v;
+            r[2 * w + half] = block_mean(k0, k1, k2, k3, n);
         }
     }
     // block-key row in [num_pages][Hkv][page_size / 4][256]

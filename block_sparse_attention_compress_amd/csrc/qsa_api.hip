@@ -151,8 +151,23 @@ int qsa_block_scores(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, co
     // more rows than sequences: rows share block keys, score them as a matrix product
     const bool tiled = q_seq && R > p.batch;
     hipError_t e = tiled ? qsa::launch_scores_tiled(p, rows, scores, score_stride, st)
-                         : qsa::launch_scores_stream(p, rows, scores, score_stride, st);
+                         : qsa::launch_scores_stream(p, rows, scores, score_stride, false, st);
     return hip_status(e, "qsa_block_scores");
+}
+
+int qsa_decode_scores_refresh(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq, float* scores,
+                              int32_t score_stride, void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, true, false, true, &p)) return rc;
+    if (int rc = check_heads(Hq, p.Hkv)) return rc;
+    if (int rc = check_q(q, q_row_stride, Hq)) return rc;
+    if (!scores) return fail(QSA_ERR_INVALID_ARG, "scores is NULL");
+    if (score_stride < 1 || score_stride > QSA_MAX_SEQ_LEN / QSA_MICROBLOCK)
+        return fail(QSA_ERR_INVALID_ARG, "score_stride %d out of [1, %d]", score_stride,
+                    QSA_MAX_SEQ_LEN / QSA_MICROBLOCK);
+    qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, nullptr, nullptr, p.batch, Hq};
+    return hip_status(qsa::launch_scores_stream(p, rows, scores, score_stride, true, static_cast<hipStream_t>(stream)),
+                      "qsa_decode_scores_refresh");
 }
 
 static int check_topk(const float* scores, int32_t score_stride, int32_t R, int32_t Hkv, int32_t k,

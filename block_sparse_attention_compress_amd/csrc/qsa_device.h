@@ -26,6 +26,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Block key element: the fp32 mean of the first n (1..4) of a block's keys,
+// ((k0 + k1) + (k2 + k3)) * 0.25 for a full block, the left-to-right sum divided
+// by n (correctly rounded) for a partial last block.
+__device__ __forceinline__ float block_mean(float k0, float k1, float k2, float k3, int n) {
+    if (n == 4) {
+        const float s01 = k0 + k1;
+        const float s23 = k2 + k3;
+        return (s01 + s23) * 0.25f;
+    }
+    if (n == 3) return __fdiv_rn((k0 + k1) + k2, 3.0f);
+    if (n == 2) return (k0 + k1) * 0.5f;  // exact halving == division by 2
+    return k0;
+}
+
 // Row index (in 256-element rows) of token `pos` of sequence `seq`, KV head h,
 // in a paged [num_pages][Hkv][page_size][256] pool.
 __device__ __forceinline__ int64_t token_row(const int32_t* __restrict__ block_table, int seq, int max_pages,

@@ -29,7 +29,8 @@ struct Rows {
 // span: host bound on the tokens per sequence from first_token on
 hipError_t launch_compress(const PagedKV& kv, const int32_t* first_token, int span, hipStream_t st);
 
-hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
+// refresh: decode rows only; also rebuilds the block key holding each sequence's newest token
+hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scores, int score_stride, bool refresh,
                                 hipStream_t st);
 hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
                                hipStream_t st);

@@ -26,23 +26,39 @@ constexpr int kGroups = kStreamChunk / 64;  // 16-block groups per wave
 // BF16: block keys are bf16 (8 bytes per lane and block instead of 16); they
 // are kept raw until the dot product, so the next group's loads still fly
 // while a group is reduced.
+// REFRESH: the wave named by `rf` first rebuilds one block key from the K cache
+// (the block holding a sequence's newest token), stores it, and scores that
+// block with it in place of the stored, stale key.
 template <bool BF16>
 struct KeyRaw {
     typedef float4 type;
+    static __device__ __forceinline__ float4 from(const float4& m) { return m; }
 };
 template <>
 struct KeyRaw<true> {
     typedef uint2 type;
+    static __device__ __forceinline__ uint2 from(const float4& m) {
+        return make_uint2(pack_bf16x2(m.x, m.y), pack_bf16x2(m.z, m.w));
+    }
+};
+
+struct Refresh {
+    const uint16_t* k = nullptr;  // K cache [num_pages][Hkv][page_size][256]
+    void* ckey = nullptr;         // block keys, written
+    int b = -1;                   // block to rebuild (-1: none in this wave)
+    int n = 0;                    // its tokens, 1..4
+    bool score = false;           // b is one of the blocks this wave scores
+    float4* stash = nullptr;      // this wave's 64 x 16 bytes of LDS: the rebuilt key until it is scored
 };
 __device__ __forceinline__ float4 key4(const float4& x) { return x; }
 __device__ __forceinline__ float4 key4(const uint2& x) {
     return make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
 }
 
-template <bool PAGE16, bool COHERENT = false, bool BF16 = false>
-__device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int g, const void* __restrict__ ckey,
+template <bool PAGE16, bool COHERENT = false, bool BF16 = false, bool REFRESH = false>
+__device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int g, const void* ckey,
                                           const int32_t* __restrict__ bt, int Hkv, int h, int lg_ps, int n_elig,
-                                          int wb0, int lane, float* __restrict__ srow) {
+                                          int wb0, int lane, float* __restrict__ srow, const Refresh& rf = Refresh{}) {
     typedef typename KeyRaw<BF16>::type Raw;
     const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
     const int lg_bpp = lg_ps - 2;  // blocks per page = page_size / 4
@@ -76,6 +92,27 @@ __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int
     Raw v[16];
     load_group(0, v);
 
+    if (REFRESH && rf.b >= 0) {
+        // the block's tokens are consecutive rows of one page; lane: dims 4 lane .. 4 lane + 3
+        const int64_t pos0 = 4 * (int64_t)rf.b;
+        const int64_t row = (((int64_t)bt[pos0 >> lg_ps] * Hkv + h) << lg_ps) + (pos0 & ((1 << lg_ps) - 1));
+        const uint2* src = reinterpret_cast<const uint2*>(rf.k + row * kHeadDim) + lane;
+        uint2 a[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = u < rf.n ? src[u * (kHeadDim / 4)] : make_uint2(0, 0);
+        float4 m;
+        m.x = block_mean(bf16_lo(a[0].x), bf16_lo(a[1].x), bf16_lo(a[2].x), bf16_lo(a[3].x), rf.n);
+        m.y = block_mean(bf16_hi(a[0].x), bf16_hi(a[1].x), bf16_hi(a[2].x), bf16_hi(a[3].x), rf.n);
+        m.z = block_mean(bf16_lo(a[0].y), bf16_lo(a[1].y), bf16_lo(a[2].y), bf16_lo(a[3].y), rf.n);
+        m.w = block_mean(bf16_hi(a[0].y), bf16_hi(a[1].y), bf16_hi(a[2].y), bf16_hi(a[3].y), rf.n);
+        const Raw fresh = KeyRaw<BF16>::from(m);
+        // block-key row in [num_pages][Hkv][page_size / 4][256]
+        const int64_t brow = ((row >> lg_ps) << (lg_ps - 2)) + ((row & ((1 << lg_ps) - 1)) >> 2);
+        reinterpret_cast<Raw*>(rf.ckey)[brow * (kHeadDim / 4) + lane] = fresh;
+        // parked in LDS rather than held in registers through the loop
+        if (rf.score) reinterpret_cast<Raw*>(rf.stash)[lane] = fresh;
+    }
+
     // group-summed query: lane holds dims 4*lane .. 4*lane+3; the g loads are
     // issued together (one wait), summed in head order
     float4 qs = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -96,11 +133,19 @@ __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int
     for (int grp = 0; grp < kGroups; ++grp) {
         const int b0 = wb0 + grp * 16;
         if (b0 >= n_elig) break;
+        if (REFRESH && rf.score && ((rf.b - wb0) >> 4) == grp) {
+            const int jf = (rf.b - wb0) & 15;
+            const Raw fresh = reinterpret_cast<const Raw*>(rf.stash)[lane];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (j == jf) v[j] = fresh;
+        }
+        // explicit fused multiply-adds: every instantiation rounds the same way
         float p[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const float4 kv = key4(v[j]);
-            p[j] = qs.x * kv.x + qs.y * kv.y + qs.z * kv.z + qs.w * kv.w;
+            p[j] = fmaf(qs.w, kv.w, fmaf(qs.z, kv.z, fmaf(qs.y, kv.y, qs.x * kv.x)));
         }
         // the next group's loads fly while this group is reduced
         if (grp < kGroups - 1 && b0 + 16 < n_elig) load_group(grp + 1, v);

@@ -22,12 +22,12 @@
 
 namespace qsa {
 
-template <bool PAGE16, bool BF16>
+template <bool PAGE16, bool BF16, bool REFRESH>
 __global__ __launch_bounds__(256) void scores_stream_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int g, const void* __restrict__ ckey, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ q_pos, int g, const void* ckey, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages, float* __restrict__ scores,
-    int score_stride) {
+    int score_stride, const uint16_t* __restrict__ kcache) {
     const int row = blockIdx.z;
     const int h = blockIdx.y;
     const int seq = q_seq ? q_seq[row] : row;
@@ -41,9 +41,25 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
     const int wave = wave_id();
     const int wb0 = chunk0 + wave * (kStreamChunk / 4);  // this wave's first block
     if (wb0 >= n_elig) return;
-    scan_wave<PAGE16, false, BF16>(q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim, g, ckey,
-                      block_table + (int64_t)seq * max_pages, Hkv, h, lg_ps, n_elig, wb0, lane,
-                      scores + ((int64_t)row * Hkv + h) * score_stride);
+    __shared__ float4 stash[REFRESH ? 4 * 64 : 1];
+    Refresh rf;
+    if (REFRESH) {
+        // decode rows (t = L - 1): the newest token's block is rebuilt by the wave
+        // that scores it, or by the row's first wave when the row is cut short
+        const int b = t >> 2;
+        const bool scored = b < n_elig;
+        if (scored ? (wb0 <= b && b < wb0 + kStreamChunk / 4) : wb0 == 0) {
+            rf.k = kcache;
+            rf.ckey = const_cast<void*>(ckey);
+            rf.b = b;
+            rf.n = L - 4 * b;
+            rf.score = scored;
+            rf.stash = stash + wave * 64;
+        }
+    }
+    scan_wave<PAGE16, false, BF16, REFRESH>(q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim, g, ckey,
+                                            block_table + (int64_t)seq * max_pages, Hkv, h, lg_ps, n_elig, wb0, lane,
+                                            scores + ((int64_t)row * Hkv + h) * score_stride, rf);
 }
 
 // Extend: 64 rows per workgroup, 16 per wave, and kTiledChunk blocks per
@@ -262,23 +278,31 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
     }
 }
 
-hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
+hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scores, int score_stride, bool refresh,
                                 hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
     dim3 grid((score_stride + kStreamChunk - 1) / kStreamChunk, kv.Hkv, rows.R);
     const bool page16 = kv.lg_ps >= 6;
-#define QSA_SCAN(P16, B16)                                                                                      \
-    hipLaunchKernelGGL((scores_stream_kernel<P16, B16>), grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq, \
-                       rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps,     \
-                       kv.max_pages, scores, score_stride)
+#define QSA_SCAN(P16, B16, RF)                                                                                     \
+    hipLaunchKernelGGL((scores_stream_kernel<P16, B16, RF>), grid, dim3(256), 0, st, rows.q, rows.q_stride,         \
+                       rows.q_seq, rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv,      \
+                       kv.lg_ps, kv.max_pages, scores, score_stride, kv.k)
+#define QSA_SCAN_RF(P16, B16)  \
+    do {                       \
+        if (refresh)           \
+            QSA_SCAN(P16, B16, true); \
+        else                   \
+            QSA_SCAN(P16, B16, false); \
+    } while (0)
     if (page16 && kv.ckey_bf16)
-        QSA_SCAN(true, true);
+        QSA_SCAN_RF(true, true);
     else if (page16)
-        QSA_SCAN(true, false);
+        QSA_SCAN_RF(true, false);
     else if (kv.ckey_bf16)
-        QSA_SCAN(false, true);
+        QSA_SCAN_RF(false, true);
     else
-        QSA_SCAN(false, false);
+        QSA_SCAN_RF(false, false);
+#undef QSA_SCAN_RF
 #undef QSA_SCAN
     return hipGetLastError();
 }

@@ -11,7 +11,7 @@ from typing import Optional
 
 import torch
 
-from . import (HEAD_DIM, KVCache, qsa_block_scores, qsa_compress_keys, qsa_decode_fused,
+from . import (HEAD_DIM, KVCache, qsa_block_scores, qsa_compress_keys, qsa_decode_fused, qsa_decode_scores_refresh,
                qsa_decode_fused_workspace_bytes, qsa_decode_workspace_bytes, qsa_sparse_attn_decode,
                qsa_sparse_attn_extend, qsa_topk_blocks, qsa_topk_blocks_ws, qsa_topk_workspace_bytes)
 
@@ -49,13 +49,14 @@ class DecodeBuffers:
 def decode_step(kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: DecodeBuffers, scale: float = 0.0,
                 num_splits: int = 0, refresh_keys: bool = True, stream=None) -> None:
     """One decode step for every sequence of `kv`: refresh the block key holding the
-    newest token (q_pos = L - 1), score, select, attend (and merge the splits).
-    q: bf16 [B][Hq][256] (rows may be strided)."""
+    newest token and score (one launch), select, attend (and merge the splits).
+    q: bf16 [B][Hq][256] (rows may be strided); q_pos = L - 1 per sequence."""
     B, Hq = q.shape[0], q.shape[1]
     Hkv = kv.k.shape[1]
     if refresh_keys:
-        qsa_compress_keys(kv, q_pos, 1, stream=stream)
-    qsa_block_scores(kv, q, q.stride(0), None, None, B, Hq, buf.scores, buf.score_stride, stream=stream)
+        qsa_decode_scores_refresh(kv, q, q.stride(0), Hq, buf.scores, buf.score_stride, stream=stream)
+    else:
+        qsa_block_scores(kv, q, q.stride(0), None, None, B, Hq, buf.scores, buf.score_stride, stream=stream)
     tw = buf.topk_workspace
     qsa_topk_blocks_ws(buf.scores, buf.score_stride, q_pos, B, Hkv, buf.k, buf.sel_idx, buf.sel_cnt, workspace=tw,
                        workspace_bytes=0 if tw is None else tw.numel(), stream=stream)
@@ -143,8 +144,8 @@ def extend_step(kv: KVCache, q: torch.Tensor, q_seq: torch.Tensor, q_pos: torch.
 class DecodeGraph:
     """A decode step captured once in a HIP graph and replayed.
 
-    The library never allocates, synchronises or memsets, so the five launches of
-    a step record as plain kernel nodes.  Inputs are read from the buffers given at
+    The library never allocates, synchronises or memsets, so the launches of a
+    step record as plain kernel nodes.  Inputs are read from the buffers given at
     capture time: update them in place (q, q_pos, the cache) between replays."""
 
     def __init__(self, kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: DecodeBuffers, scale: float = 0.0,

@@ -136,6 +136,21 @@ QSA_API int qsa_block_scores(const qsa_kv_t* kv, const void* q, int64_t q_row_st
                      void* stream);
 
 /*
+ * a1 + a2 for one decode step in one launch: the same results, bit for bit, as
+ *   qsa_compress_keys(kv, first_token = {L_s - 1}, 1, stream);
+ *   qsa_block_scores(kv, q, q_row_stride, NULL, NULL, batch, Hq, scores, score_stride, stream);
+ * i.e. the block key holding each sequence's newest token is rebuilt from K (and
+ * stored), and every eligible block of every row is scored, the newest one
+ * with its rebuilt key.  Sequences with L_s = 0 are skipped.  The block keys
+ * rebuilt here must not be read by another sequence of the same call (the page
+ * holding a sequence's newest token belongs to that sequence alone, as in a
+ * paged cache that copies a shared page before appending to it).  Arguments
+ * and errors as for the two calls.
+ */
+QSA_API int qsa_decode_scores_refresh(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq,
+                                      float* scores, int32_t score_stride, void* stream);
+
+/*
  * a3 -- top-k selection.  For each (row, KV head): among the n_elig(r)
  * scores (q_pos as above; NULL means n_elig = score_stride for every row),
  * keeps the k largest under the order (score descending, block index

@@ -98,6 +98,19 @@ def test_scores_head_and_stride_checks():
     assert status(L, ctypes.byref(d), P, 2048, None, None, 2, 8, P, (1 << 18) + 1, None) == qsa.QSA_ERR_INVALID_ARG
 
 
+def test_decode_scores_refresh_rejects():
+    f = qsa.lib().qsa_decode_scores_refresh
+    d = kv()
+    assert f(ctypes.byref(d), None, 4096, 16, P, 800, None) == qsa.QSA_ERR_INVALID_ARG     # q
+    assert f(ctypes.byref(d), P, 4096, 16, None, 800, None) == qsa.QSA_ERR_INVALID_ARG     # scores
+    assert f(ctypes.byref(d), P, 4096, 16, P, 0, None) == qsa.QSA_ERR_INVALID_ARG         # stride
+    assert f(ctypes.byref(d), P, 4096, 15, P, 800, None) == qsa.QSA_ERR_UNSUPPORTED       # Hq % Hkv
+    dk = kv(k=None)                                                                       # K is read
+    assert f(ctypes.byref(dk), P, 4096, 16, P, 800, None) == qsa.QSA_ERR_INVALID_ARG
+    dc = kv(ckey=None)
+    assert f(ctypes.byref(dc), P, 4096, 16, P, 800, None) == qsa.QSA_ERR_INVALID_ARG
+
+
 def test_topk_rejects():
     L = "qsa_topk_blocks"
     assert status(L, None, 100, None, 2, 2, 16, P, P, None) == qsa.QSA_ERR_INVALID_ARG
