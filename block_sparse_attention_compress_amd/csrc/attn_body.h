@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& a, int w) {
 // write of the result; the caller separates work units sharing `smem` with a
 // barrier.
 __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h, int s, float* smem) {
-    __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
+    __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16], h_inv[16], h_lse[16];
     int32_t* slot_row = reinterpret_cast<int32_t*>(smem);
     const int S = P.S;
     const int seq = P.q_seq ? P.q_seq[row] : row;
@@ -278,7 +278,10 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
 #undef QSA_LOAD_J
 #undef QSA_STAGE_J
 
-    // ---- merge the 4 waves in LDS
+    // ---- merge the 4 waves in LDS.  Per head: M = the largest reference max of
+    // the waves that saw a token; wave w's O and l are scaled by 2^(m_w - M)
+    // before the exchange, so the final pass only adds the 4 slots and
+    // multiplies by 1 / sum(l).
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     __syncthreads();  // the slot table is dead; smem becomes the O exchange
@@ -286,44 +289,78 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         wm[wave][c] = m_run;
         wl[wave][c] = l_tot;
     }
-    float* ow = smem + wave * g * kHeadDim;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (4 * qq + i < g) {
-#pragma unroll
-            for (int nt = 0; nt < 16; ++nt)
-                ow[(4 * qq + i) * kHeadDim + 128 * (nt >> 3) + 8 * c + (nt & 7)] = O[nt][i];
-        }
     __syncthreads();
-
     const float kLn2 = 0.6931471805599453f;
-    for (int e = tid; e < g * kHeadDim; e += 256) {
-        const int hh = e >> 8;
-        const int d = e & (kHeadDim - 1);
+    auto head_max = [&](int hh) {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wl[w][hh] > 0.f ? wm[w][hh] : -INFINITY);
-        float o = 0.f, lse_v = -INFINITY;
+        return M;
+    };
+    if (wave == 0 && qq == 0 && c < g) {  // one lane per head: 1 / sum(l) and the lse
+        const float M = head_max(c);
+        float den = 0.f;
         if (M != -INFINITY) {
-            float num = 0.f, den = 0.f;
 #pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) {
-                if (!(wl[w][hh] > 0.f)) continue;
-                const float f = __builtin_amdgcn_exp2f(wm[w][hh] - M);
-                num += f * smem[(w * g + hh) * kHeadDim + d];
-                den += f * wl[w][hh];
-            }
-            o = num / den;
-            lse_v = (M + __log2f(den)) * kLn2;
+            for (int w = 0; w < kAttnWaves; ++w)
+                if (wl[w][c] > 0.f) den += __builtin_amdgcn_exp2f(wm[w][c] - M) * wl[w][c];
         }
+        h_inv[c] = M != -INFINITY ? 1.0f / den : 0.f;
+        h_lse[c] = M != -INFINITY ? (M + __log2f(den)) * kLn2 : -INFINITY;
+    }
+    // this lane's O: heads 4 qq + i, dims 128 hf + 8 c + j at O[8 hf + j][i]
+    float* ow = smem + wave * g * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int hh = 4 * qq + i;
+        if (hh < g) {
+            const float M = head_max(hh);
+            const float f = wl[wave][hh] > 0.f ? __builtin_amdgcn_exp2f(wm[wave][hh] - M) : 0.f;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                float4* dst = reinterpret_cast<float4*>(ow + hh * kHeadDim + 128 * hf + 8 * c);
+                dst[0] = make_float4(O[8 * hf + 0][i] * f, O[8 * hf + 1][i] * f, O[8 * hf + 2][i] * f,
+                                     O[8 * hf + 3][i] * f);
+                dst[1] = make_float4(O[8 * hf + 4][i] * f, O[8 * hf + 5][i] * f, O[8 * hf + 6][i] * f,
+                                     O[8 * hf + 7][i] * f);
+            }
+        }
+    }
+    __syncthreads();
+
+    // thread: 4 consecutive dims of one head per pass
+    const float4* o4 = reinterpret_cast<const float4*>(smem);
+    const bool out8 = ((reinterpret_cast<uintptr_t>(P.out) | (uintptr_t)(P.out_stride * 2)) & 7) == 0;
+    for (int e = tid; e < g * (kHeadDim / 4); e += 256) {
+        const int hh = e >> 6;
+        const int d = 4 * (e & 63);
+        float4 acc = o4[hh * 64 + (e & 63)];
+#pragma unroll
+        for (int w = 1; w < kAttnWaves; ++w) {
+            const float4 x = o4[(w * g + hh) * 64 + (e & 63)];
+            acc.x += x.x;
+            acc.y += x.y;
+            acc.z += x.z;
+            acc.w += x.w;
+        }
+        const float inv = h_inv[hh];
+        const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
         const int head = h * g + hh;
         if (P.part_out) {
             const int64_t prow = ((int64_t)s * P.R + row) * P.Hq + head;
-            P.part_out[prow * kHeadDim + d] = o;
-            if (d == 0) P.part_lse[prow] = lse_v;
+            *reinterpret_cast<float4*>(P.part_out + prow * kHeadDim + d) = o;
+            if (d == 0) P.part_lse[prow] = h_lse[hh];
         } else {
-            P.out[(int64_t)row * P.out_stride + (int64_t)head * kHeadDim + d] = (uint16_t)f32_to_bf16_rne(o);
-            if (d == 0 && P.lse) P.lse[(int64_t)row * P.Hq + head] = lse_v;
+            uint16_t* dst = P.out + (int64_t)row * P.out_stride + (int64_t)head * kHeadDim + d;
+            if (out8) {
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+            } else {
+                dst[0] = (uint16_t)f32_to_bf16_rne(o.x);
+                dst[1] = (uint16_t)f32_to_bf16_rne(o.y);
+                dst[2] = (uint16_t)f32_to_bf16_rne(o.z);
+                dst[3] = (uint16_t)f32_to_bf16_rne(o.w);
+            }
+            if (d == 0 && P.lse) P.lse[(int64_t)row * P.Hq + head] = h_lse[hh];
         }
     }
 }
