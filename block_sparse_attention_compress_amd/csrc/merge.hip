@@ -8,11 +8,15 @@
 //
 // One wave per output row: lane s < S holds lse_s, the wave max / sum give M and
 // the normaliser, and each lane then accumulates 4 dims at a time with the split
-// weights broadcast from their lanes.
+// weights broadcast from their lanes.  The lane's first 16 partials are loaded
+// together with the lse, so a row costs one memory round trip when S <= 16 and
+// D <= 256.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
 namespace qsa {
+
+constexpr int kMergeBatch = 16;  // partial loads in flight per lane
 
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_out,
                                                     const float* __restrict__ part_lse, int S, int N, int D,
@@ -20,10 +24,20 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
     if (row >= N) return;
+    // the partials do not depend on the lse: their first batch is requested with it
+    const int d0 = 4 * lane;
+    float4 o[kMergeBatch];
+    auto load_batch = [&](int d, int sp0) {
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j)
+            if (sp0 + j < S && d < D)
+                o[j] = *reinterpret_cast<const float4*>(part_out + ((int64_t)(sp0 + j) * N + row) * D + d);
+    };
+    load_batch(d0, 0);
     const float ls = lane < S ? part_lse[(int64_t)lane * N + row] : -INFINITY;
     const float M = wave_max(ls);
     if (M == -INFINITY) {
-        for (int d = 4 * lane; d < D; d += 256)
+        for (int d = d0; d < D; d += 256)
             *reinterpret_cast<uint2*>(out + row * D + d) = make_uint2(0u, 0u);
         if (lane == 0 && out_lse) out_lse[row] = -INFINITY;
         return;
@@ -31,15 +45,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     const float w = lane < S ? expf(ls - M) : 0.f;
     const float z = wave_sum(w);
     const float wn = w / z;
-    for (int d = 4 * lane; d < D; d += 256) {
+    for (int d = d0; d < D; d += 256) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp = 0; sp < S; ++sp) {
-            const float ws = __shfl(wn, sp);
-            const float4 o = *reinterpret_cast<const float4*>(part_out + ((int64_t)sp * N + row) * D + d);
-            acc.x += ws * o.x;
-            acc.y += ws * o.y;
-            acc.z += ws * o.z;
-            acc.w += ws * o.w;
+        for (int sp0 = 0; sp0 < S; sp0 += kMergeBatch) {
+            if (sp0 > 0 || d > d0) load_batch(d, sp0);
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                if (sp0 + j >= S) break;
+                const float ws = __shfl(wn, sp0 + j);
+                acc.x += ws * o[j].x;
+                acc.y += ws * o[j].y;
+                acc.z += ws * o[j].z;
+                acc.w += ws * o[j].w;
+            }
         }
         *reinterpret_cast<uint2*>(out + row * D + d) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
     }
