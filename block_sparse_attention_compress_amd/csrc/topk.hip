@@ -30,16 +30,15 @@
 
 namespace qsa {
 
+// Workgroup min and max (returns max - min).  One barrier; tmp must not be
+// written again by this workgroup.
 __device__ __forceinline__ float block_min_max(float& mn, float& mx, float* tmp) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o));
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-    }
-    if (lane == 0) {
+    mn = wave_prefix_min(mn);
+    mx = wave_prefix_max(mx);
+    if (lane == 63) {
         tmp[wave] = mn;
         tmp[32 + wave] = mx;
     }
@@ -50,7 +49,6 @@ __device__ __forceinline__ float block_min_max(float& mn, float& mx, float* tmp)
         mn = fminf(mn, tmp[w]);
         mx = fmaxf(mx, tmp[32 + w]);
     }
-    __syncthreads();
     return mx - mn;
 }
 
@@ -158,6 +156,8 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
 
     const int tid = threadIdx.x;
     const int i0 = tid * KPT;  // this thread's first block
+    // the histogram is cleared while the loads fly; block_min_max's barrier orders it
+    for (int i = tid; i < kBins; i += kRegThreads) hist[i] = 0;
     // slots past n hold -inf (scores are finite): it is never selected, and
     // every test below stays a function of the value (no per-slot masks kept live)
     float v[KR];
@@ -202,8 +202,6 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     auto bin_of = [&](float x) { return (int)fminf(fmaxf((x - mn) * scale, 0.f), (float)(kBins - 1)); };
 
     // ---- pass 1: uniform bins over [mn, mx]
-    for (int i = tid; i < kBins; i += kRegThreads) hist[i] = 0;
-    __syncthreads();
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
         if (V(e) != -INFINITY) atomicAdd(&hist[bin_of(V(e))], 1);
