@@ -49,8 +49,9 @@ __device__ __forceinline__ float wave_prefix_min(float v) {
 }
 
 // Suffix sum over the block (thread t gets the sum over threads >= t) of one
-// int per thread.  tmp holds NW ints.
-template <int NW>
+// int per thread.  tmp holds NW ints.  TRAIL = false leaves out the closing
+// barrier: the caller then passes a barrier before tmp is written again.
+template <int NW, bool TRAIL = true>
 __device__ __forceinline__ int block_suffix_sum(int v, int* tmp) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -61,12 +62,13 @@ __device__ __forceinline__ int block_suffix_sum(int v, int* tmp) {
     __syncthreads();
     int after = 0;
     for (int w = wave + 1; w < NW; ++w) after += tmp[w];
-    __syncthreads();
+    if (TRAIL) __syncthreads();
     return v + after;
 }
 
 // Exclusive prefix sum over the block (thread order) of two ints per thread.
-template <int NW>
+// TRAIL as for block_suffix_sum.
+template <int NW, bool TRAIL = true>
 __device__ __forceinline__ void block_exclusive_scan2(int& a, int& b, int* tmp) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -81,7 +83,7 @@ __device__ __forceinline__ void block_exclusive_scan2(int& a, int& b, int* tmp) 
         ba += tmp[w];
         bb += tmp[NW + w];
     }
-    __syncthreads();
+    if (TRAIL) __syncthreads();
     a = ba + ia - a;
     b = bb + ib - b;
 }

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     __shared__ int cand_idx[kRegThreads];
     __shared__ int itmp[2 * kRegWaves];
     __shared__ float ftmp[64];
-    __shared__ int sh_bin, sh_above, sh_ncand, sh_need_eq;
+    __shared__ int sh_bin, sh_above, sh_ncand, sh_need_eq, sh_m;
     __shared__ uint32_t sh_T;
     constexpr int KL = KPT - KR;
     __shared__ float vl[KL > 0 ? KL * kRegThreads : 1];
@@ -208,15 +208,17 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     __syncthreads();
     {
         const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
-        const int incl = block_suffix_sum<kRegWaves>(h0 + h1, itmp);
+        const int incl = block_suffix_sum<kRegWaves, false>(h0 + h1, itmp);
         const int above = incl - h0 - h1;
         if (above < k && k <= incl) {
             if (above + h1 >= k) {
                 sh_bin = 2 * tid + 1;
                 sh_above = above;
+                sh_m = h1;
             } else {
                 sh_bin = 2 * tid;
                 sh_above = above + h1;
+                sh_m = h0;
             }
         }
         if (tid == 0) sh_ncand = 0;
@@ -224,7 +226,9 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     }
     const int B = sh_bin;
     const int need = k - sh_above;  // how many of bin B's elements are taken (>= 1)
-    const int m = hist[B];
+    // bin B's size, from a copy: the crowded path below clears hist with no barrier
+    // between this read and the clear
+    const int m = sh_m;
 
     if (m <= kRegThreads) {
         // ---- rank the bin's candidates directly
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
             }
             __syncthreads();
             const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
-            const int incl = block_suffix_sum<kRegWaves>(h0 + h1, itmp);
+            const int incl = block_suffix_sum<kRegWaves, false>(h0 + h1, itmp);
             const int above = incl - h0 - h1;
             if (above < remaining && remaining <= incl) {
                 if (above + h1 >= remaining) {
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
         gt += real && key > T;
         eq += real && key == T;
     }
-    block_exclusive_scan2<kRegWaves>(gt, eq, itmp);
+    block_exclusive_scan2<kRegWaves, false>(gt, eq, itmp);  // last use of itmp
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         if (V(e) == -INFINITY) continue;
