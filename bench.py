@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--graph", action="store_true", help="time a replayed HIP graph of the step instead of eager launches")
     p.add_argument("--splits", type=int, default=None, help="decode split count (default: the library's choice)")
     p.add_argument("--no-fused", action="store_true", help="skip the single-launch fused step figures")
+    p.add_argument("--flush", action="store_true",
+                   help="also time single steps after a 1 GiB read that evicts the caches (MALL included)")
     p.add_argument("--ckey", choices=["fp32", "bf16"], default="fp32",
                    help="block-key storage (fp32: the method's definition; bf16: the rounded-mean variant)")
     return p.parse_args()
@@ -159,7 +161,7 @@ def cpu_baseline(case, target_s: float):
                       f"the {case.B}-sequence workload, {reps} repetitions in {dt:.2f} s, block keys precomputed"}
 
 
-def extend_figures(steps: int):
+def extend_figures(steps: int, flush: bool = False):
     """Extend chunk: 4096 new query tokens on 28672 cached (32768 total), (12, 1) heads."""
     import torch
 
@@ -182,6 +184,21 @@ def extend_figures(steps: int):
         extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, first, case.R, scale=case.scale)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
+    cold = None
+    if flush:  # a 1 GiB read before each chunk evicts L2 and the MALL
+        import numpy as np
+        junk = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        ms = []
+        for i in range(steps):
+            junk.sum()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, first, case.R, scale=case.scale)
+            c1.record()
+            torch.cuda.synchronize()
+            ms.append(c0.elapsed_time(c1))
+        del junk
+        cold = round(float(np.median(ms)), 4)
     # MFMA work: scores 2*256 per eligible block per row; attention 2 * 2 * 256 per
     # (selected token, real head)
     elig = sum(min(int(t) // 4 + 1, stride) for t in case.q_pos)
@@ -189,7 +206,7 @@ def extend_figures(steps: int):
     flops = 2 * 256 * elig + 4 * 256 * case.Hq * int(cnt.sum()) * 4
     return {"workload": "extend: 4096 new tokens on 28672 cached, (12,1) heads, top-512 per query",
             "new_tokens_per_s": round(case.R / dt, 1), "ms_per_chunk": round(dt * 1e3, 4),
-            "tflops": round(flops / dt / 1e12, 2)}
+            "tflops": round(flops / dt / 1e12, 2), "cold_cache_ms_per_chunk_median": cold}
 
 
 def main():
@@ -287,6 +304,26 @@ def main():
         ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
         mode = "hip-graph replay"
 
+    # (3b) optionally, cold-cache steps: a 1 GiB read before each one evicts L2 and
+    # the 256 MB MALL (a read, so no dirty lines are left to write back during the
+    # step); HIP events bracket the step alone (median reported)
+    cold = None
+    if args.flush:
+        junk = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        cold_ms = []
+        for i in range(args.steps):
+            junk.sum()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            decode_step(kv, q, q_pos, buf, scale=case.scale, num_splits=splits)
+            c1.record()
+            torch.cuda.synchronize()
+            cold_ms.append(c0.elapsed_time(c1))
+        del junk
+        cm = float(np.median(cold_ms))
+        cold = {"ms_per_step_median": round(cm, 4), "queries_per_s": round(case.B / (cm / 1e3), 1),
+                "flush_bytes_read": 1 << 30}
+
     # (4) the fused single-launch step (qsa_decode_fused), reported beside the
     # headline; its selection must equal the separate calls'
     fused = None
@@ -343,10 +380,11 @@ def main():
                  "event_ms": {"refresh_and_scores": round(part_ms[0], 5), "topk": round(part_ms[1], 5),
                               "attention_and_merge": round(part_ms[2], 5)},
                  "execution": mode, "eager_ms_per_step": round(eager_ms, 4), "fused_single_launch": fused,
+                 "cold_cache": cold,
                  "full_block_key_build_ms": round(compress_full_ms, 4)},
     }
     if not args.no_extend:
-        result["extend"] = extend_figures(max(3, args.steps // 4))
+        result["extend"] = extend_figures(max(3, args.steps // 4), args.flush)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
