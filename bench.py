@@ -138,8 +138,19 @@ def decode_bytes(case, sel, cnt, page_size):
     return step, scores, tokens
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, target_s: float):
-    """The CPU oracle as it stands, timed on a sample of the same workload."""
+    """The CPU oracle as it stands, timed on a sample of the same workload: on
+    every host thread it may use, and on one thread (a shorter sample)."""
     import oracle
 
     threads = oracle.default_threads()
@@ -148,17 +159,25 @@ def cpu_baseline(case, target_s: float):
     data.prefetch([case.q_seq[r] for r in rows], threads)      # logical K and block keys: not timed
     for r in rows:
         data.V(int(case.q_seq[r]))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.run_case(case, rows=rows, threads=threads, data=data, keep_scores=False)
-        reps += 1
-        if time.perf_counter() - t0 >= target_s:
-            break
-    dt = time.perf_counter() - t0
+
+    def timed(rows_, nthreads, span):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.run_case(case, rows=rows_, threads=nthreads, data=data, keep_scores=False)
+            reps += 1
+            if time.perf_counter() - t0 >= span:
+                break
+        return reps, time.perf_counter() - t0
+
+    reps, dt = timed(rows, threads, target_s)
+    reps1, dt1 = timed(rows[:1], 1, max(1.0, target_s / 4))
     return {"value": round(reps * len(rows) / dt, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle decode step (scores, top-512, attention) on sequences 0..{len(rows) - 1} of "
-                      f"the {case.B}-sequence workload, {reps} repetitions in {dt:.2f} s, block keys precomputed"}
+                      f"the {case.B}-sequence workload, {reps} repetitions in {dt:.2f} s, block keys precomputed",
+            "single_thread_value": round(reps1 / dt1, 3),
+            "single_thread_sample": f"sequence 0 on 1 thread, {reps1} repetitions in {dt1:.2f} s",
+            "cpu_model": cpu_model()}
 
 
 def extend_figures(steps: int, flush: bool = False):

@@ -18,15 +18,17 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("num_splits", [0, 1, 4])
-def test_graph_replays_match_eager(num_splits):
-    case = synth.config("C2", B=6, L_range=(9000, 17000))
-    log(f"graph replay, num_splits={num_splits}")
+@pytest.mark.parametrize("num_splits,L_range", [(0, (9000, 17000)), (1, (9000, 17000)), (4, (9000, 17000)),
+                                                (0, (70000, 90000))])  # rows over 16,384 blocks: two-stage top-k
+def test_graph_replays_match_eager(num_splits, L_range):
+    case = synth.config("C2", B=6, L_range=L_range)
+    log(f"graph replay, num_splits={num_splits}, lengths {L_range}")
     dev = synth.to_device(case, "cuda")
     kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
     qsa.qsa_compress_keys(kv)
     stride = max(case.nb(i) for i in range(case.B))
     buf = DecodeBuffers.allocate(case.B, case.Hq, case.Hkv, stride, case.topk, num_splits, "cuda")
+    assert (buf.topk_workspace is not None) == (stride > 16384)
     decode_step(kv, dev["q"], dev["q_pos"], buf, scale=case.scale, num_splits=num_splits)
     torch.cuda.synchronize()
     want = (buf.sel_idx.clone(), buf.sel_cnt.clone(), buf.out.clone(), buf.lse.clone())
