@@ -61,6 +61,7 @@ def lib():
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         L.oracle_compress.argtypes = [vp, i64, i32, vp]
         L.oracle_compress_bf16.argtypes = [vp, i64, i32, vp]
+        L.oracle_compress_fp8.argtypes = [vp, i64, i32, vp, vp]
         L.oracle_scores.argtypes = [vp, i32, i32, vp, i64, vp]
         L.oracle_topk.argtypes = [vp, i64, i32, vp, vp]
         L.oracle_attend.argtypes = [vp, i32, i32, vp, vp, i64, i64, vp, i32, dbl, i32, i32, vp, vp]
@@ -85,16 +86,29 @@ def _check(rc: int, what: str):
 
 def compress(keys: np.ndarray, ckey_dtype: str = "fp32") -> np.ndarray:
     """keys bf16 bits [L][D] -> block keys float32 [ceil(L/4)][D]; with
-    ckey_dtype "bf16", the fp32 means rounded to bf16 (returned as float32)."""
+    ckey_dtype "bf16" / "fp8", the fp32 means rounded to bf16 / fp8 E4M3
+    (returned decoded to float32)."""
     keys = np.ascontiguousarray(keys, dtype=np.uint16)
     L, D = keys.shape
     out = np.empty(((L + 3) // 4, D), dtype=np.float32)
     if ckey_dtype == "bf16":
         _check(lib().oracle_compress_bf16(_p(keys), L, D, _p(out)), "oracle_compress_bf16")
+    elif ckey_dtype == "fp8":
+        _check(lib().oracle_compress_fp8(_p(keys), L, D, _p(out), None), "oracle_compress_fp8")
     else:
         assert ckey_dtype == "fp32", ckey_dtype
         _check(lib().oracle_compress(_p(keys), L, D, _p(out)), "oracle_compress")
     return out
+
+
+def compress_fp8_codes(keys: np.ndarray) -> np.ndarray:
+    """keys bf16 bits [L][D] -> fp8 E4M3 block-key codes uint8 [ceil(L/4)][D]."""
+    keys = np.ascontiguousarray(keys, dtype=np.uint16)
+    L, D = keys.shape
+    out = np.empty(((L + 3) // 4, D), dtype=np.float32)
+    codes = np.empty(((L + 3) // 4, D), dtype=np.uint8)
+    _check(lib().oracle_compress_fp8(_p(keys), L, D, _p(out), _p(codes)), "oracle_compress_fp8")
+    return codes
 
 
 def scores(q_group: np.ndarray, ckey: np.ndarray, n_elig: int) -> np.ndarray:

@@ -106,6 +106,50 @@ int oracle_compress_bf16(const uint16_t* keys, int64_t L, int32_t D, float* ckey
     return 0;
 }
 
+/* ------------------------------------------------------------------ O1c
+ * fp8 block keys, the same source as O1b: OCP E4M3 ("fn": sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, largest finite value 448, no infinities).  An
+ * fp8 block key is the O1 fp32 mean rounded to the nearest E4M3 value, ties to
+ * the even code; a mean whose magnitude rounds past 448 is held at 448 (the
+ * saturating conversion fp8 caches use, so no key becomes NaN).  The decoded
+ * value (exact in fp32) feeds O2 unchanged; the codes are what the cache holds. */
+static uint8_t e4m3_encode(float x) {
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs((double)x);
+    if (a >= 448.0) return sign | 0x7E;                  /* saturate */
+    if (a < 0.015625) {                                  /* below 2^-6: steps of 2^-9 */
+        const double q = nearbyint(a * 512.0);           /* 0..8; 8 is 2^-6, code 0x08 */
+        return sign | (uint8_t)q;
+    }
+    int e;
+    const double m = frexp(a, &e);                       /* a = m 2^e, m in [0.5, 1) */
+    int E = e - 1;                                       /* a = (2m) 2^E, 2m in [1, 2) */
+    double q = nearbyint((2.0 * m - 1.0) * 8.0);         /* 3-bit fraction, ties to even */
+    if (q == 8.0) {
+        q = 0.0;
+        E += 1;
+    }
+    return sign | (uint8_t)(((E + 7) << 3) | (int)q);
+}
+
+static float e4m3_decode(uint8_t c) {
+    const int E = (c >> 3) & 15, M = c & 7;
+    const double v = E ? ldexp(8.0 + M, E - 10) : ldexp((double)M, -9);
+    return (float)((c & 0x80) ? -v : v);
+}
+
+int oracle_compress_fp8(const uint16_t* keys, int64_t L, int32_t D, float* ckey, uint8_t* codes) {
+    int rc = oracle_compress(keys, L, D, ckey);
+    if (rc) return rc;
+    const int64_t nb = (L + 3) / 4;
+    for (int64_t i = 0; i < nb * D; ++i) {
+        const uint8_t c = e4m3_encode(ckey[i]);
+        if (codes) codes[i] = c;
+        ckey[i] = e4m3_decode(c);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ O2
  * Block scores of one (row, KV head): q [g][D] bf16 holds the g query heads
  * of the group; s[b] = sum_d (sum_j q[j][d]) * ckey[b][d] for b < n_elig,

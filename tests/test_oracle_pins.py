@@ -103,6 +103,47 @@ def test_o1_tail_divisor_three():
     assert oracle.compress(keys)[0, 0] == frac_to_f32(Fraction(5, 3))
 
 
+def test_o1c_fp8_block_keys_match_torch_e4m3fn():
+    """O1c: within range, the fp8 block key is torch's float32 -> float8_e4m3fn
+    conversion (round to nearest, ties to even) of the O1 mean: codes and decoded
+    values, signed zeros and subnormal steps included (catches the bias-8 variant,
+    truncation, or rounding the keys before the mean)."""
+    for L, scale in ((64, 3.0), (61, 0.02), (7, 1.0), (1, 0.004), (4099, 2.0)):
+        keys = rand_bf16((L, 256), scale=scale)
+        mean = oracle.compress(keys)
+        t = torch.from_numpy(mean).to(torch.float8_e4m3fn)
+        codes = oracle.compress_fp8_codes(keys)
+        assert codes.dtype == np.uint8 and codes.shape == mean.shape
+        assert np.array_equal(codes, t.view(torch.uint8).numpy()), (L, scale)
+        got = oracle.compress(keys, "fp8")
+        assert np.array_equal(got.view(np.uint32), t.to(torch.float32).numpy().view(np.uint32)), (L, scale)
+
+
+def test_o1c_saturation_ties_and_signed_zero():
+    """O1c closed forms: means at or past 448 are held at +-448 (code 0x7E / 0xFE;
+    torch would give NaN there); halfway means go to the even code in the normal
+    and the subnormal range; the smallest normal 2^-6 is reached by rounding up; an
+    all -0 block stays -0 (code 0x80)."""
+    def block(vals):
+        keys = np.zeros((4, 256), dtype=np.float32)
+        keys[:, 0] = vals
+        k = f32_to_bf16(keys)
+        return oracle.compress_fp8_codes(k)[0, 0], oracle.compress(k, "fp8")[0, 0]
+
+    assert block([1000.0] * 4) == (0x7E, np.float32(448.0))
+    assert block([-1.0e4] * 4) == (0xFE, np.float32(-448.0))
+    assert block([464.0] * 4) == (0x7E, np.float32(448.0))      # tie between 448 and 480: even code
+    assert block([460.0] * 4) == (0x7E, np.float32(448.0))
+    assert block([1.0625] * 4) == (0x38, np.float32(1.0))       # tie between 1 and 1.125 -> 1
+    assert block([1.1875] * 4) == (0x3A, np.float32(1.25))      # tie between 1.125 and 1.25 -> 1.25
+    assert block([1.5 * 2.0 ** -9] * 4) == (0x02, np.float32(2.0 ** -8))   # subnormal tie -> even
+    assert block([2.0 ** -10] * 4) == (0x00, np.float32(0.0))              # half the smallest step -> 0
+    assert block([0.75 * 2.0 ** -9] * 4) == (0x01, np.float32(2.0 ** -9))
+    assert block([2.0 ** -7 * 1.9921875] * 4) == (0x08, np.float32(2.0 ** -6))
+    c, v = block([-0.0] * 4)
+    assert c == 0x80 and v == 0.0 and np.signbit(v)
+
+
 # --------------------------------------------------------------------------- O2
 
 def test_o1b_bf16_block_keys_match_torch_rounding():
