@@ -57,8 +57,8 @@ def parse():
     p.add_argument("--no-fused", action="store_true", help="skip the single-launch fused step figures")
     p.add_argument("--flush", action="store_true",
                    help="also time single steps after a 1 GiB read that evicts the caches (MALL included)")
-    p.add_argument("--ckey", choices=["fp32", "bf16"], default="fp32",
-                   help="block-key storage (fp32: the method's definition; bf16: the rounded-mean variant)")
+    p.add_argument("--ckey", choices=["fp32", "bf16", "fp8"], default="fp32",
+                   help="block-key storage (fp32: the method's definition; bf16 / fp8: the rounded-mean variants)")
     return p.parse_args()
 
 
@@ -82,6 +82,8 @@ def describe(case) -> str:
         extra.append(f"{case.splits} split-KV partitions merged by log-sum-exp")
     if case.ckey_dtype == "bf16":
         extra.append("bf16 block keys (fp32 means rounded to nearest even)")
+    if case.ckey_dtype == "fp8":
+        extra.append("fp8 E4M3 block keys (fp32 means rounded to nearest even, held at +-448)")
     return (f"{case.name}: decode, {case.B} sequence{'s' if case.B > 1 else ''}, {lens}, ({case.Hq},{case.Hkv}) heads, "
             f"head_dim 256, {cache}, top-{case.topk} microblocks of 4" + "".join("; " + e for e in extra))
 
@@ -110,7 +112,7 @@ def decode_bytes(case, sel, cnt, page_size):
     """Algorithmic HBM bytes of one decode step, and of its refresh-and-score launch.
 
     step: per (sequence, KV head) the block-key scan (nb * 1 KiB for fp32 keys,
-    nb * 512 B for bf16 keys), the rebuilt newest block key (its 1..4 bf16 K rows
+    nb * 512 B for bf16 keys, nb * 256 B for fp8 keys), the rebuilt newest block key (its 1..4 bf16 K rows
     read, one block key written) and the bf16 K and V rows of the selected tokens
     (512 B each), plus q and out rows (bf16), lse (fp32), the block table and the
     lengths.
@@ -120,7 +122,7 @@ def decode_bytes(case, sel, cnt, page_size):
 
     B, Hkv, Hq = case.B, case.Hkv, case.Hq
     nb = np.array([case.nb(i) for i in range(B)], dtype=np.int64)
-    key_bytes = 256 * (2 if case.ckey_dtype == "bf16" else 4)
+    key_bytes = 256 * {"bf16": 2, "fp8": 1}.get(case.ckey_dtype, 4)
     ckey = int(nb.sum()) * Hkv * key_bytes
     refresh = sum((int(L) - 4 * ((int(L) - 1) // 4)) * 512 + key_bytes for L in case.lens if L > 0) * Hkv
     tokens = 0

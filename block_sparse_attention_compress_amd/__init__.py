@@ -35,6 +35,7 @@ MAX_TOPK = 2048
 MAX_SPLITS = 64
 CKEY_FP32 = 0
 CKEY_BF16 = 1
+CKEY_FP8 = 2
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks",
            "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse",
@@ -142,10 +143,11 @@ class KVCache:
 
     def descriptor(self) -> qsa_kv_t:
         num_pages, hkv, page_size, d = self.k.shape
-        bf16 = self.ckey is not None and str(getattr(self.ckey, "dtype", "")) == "torch.bfloat16"
+        dt = str(getattr(self.ckey, "dtype", "")) if self.ckey is not None else ""
+        ckey_dtype = {"torch.bfloat16": CKEY_BF16, "torch.float8_e4m3fn": CKEY_FP8}.get(dt, CKEY_FP32)
         return qsa_kv_t(_ptr(self.k), _ptr(self.v), _ptr(self.ckey), _ptr(self.block_table), _ptr(self.seq_lens),
                         int(self.block_table.shape[0]), int(hkv), int(d), int(page_size), int(num_pages),
-                        int(self.block_table.shape[1]), int(self.max_seq_len), CKEY_BF16 if bf16 else CKEY_FP32)
+                        int(self.block_table.shape[1]), int(self.max_seq_len), ckey_dtype)
 
 
 def _kv(kv) -> qsa_kv_t:

@@ -11,15 +11,16 @@
 // one holding first_token, so a decode refresh launches one chunk per
 // (sequence, KV head).  Thread t handles
 // microblock t/16 of the chunk and dims 16*(t%16) .. +15: four 32-byte key reads,
-// one 64-byte block-key write (32 bytes for bf16 block keys, which store the
-// same mean rounded to nearest, ties to even).  A pure HBM stream (read 2 B,
-// write 1 B -- 0.5 B for bf16 -- per key element of a block).
+// one 64-byte block-key write (32 bytes for bf16 block keys, 16 for fp8 E4M3
+// ones, which store the same mean rounded to nearest, ties to even, fp8 held at
+// +-448).  A pure HBM stream (read 2 B, write 1 B -- 0.5 B for bf16, 0.25 B for
+// fp8 -- per key element of a block).
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
 namespace qsa {
 
-template <bool BF16>
+template <int KT>
 __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restrict__ k, void* __restrict__ ckey,
                                                        const int32_t* __restrict__ block_table,
                                                        const int32_t* __restrict__ seq_lens,
@@ -70,7 +71,11 @@ __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restric
     }
     // block-key row in [num_pages][Hkv][page_size / 4][256]
     const int64_t brow = ((row >> lg_ps) << (lg_ps - 2)) + ((row & ((1 << lg_ps) - 1)) >> 2);
-    if (BF16) {
+    if (KT == kKeyFP8) {
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(ckey) + brow * kHeadDim + 16 * e);
+        *dst = make_uint4(pack_fp8x4(r[0], r[1], r[2], r[3]), pack_fp8x4(r[4], r[5], r[6], r[7]),
+                          pack_fp8x4(r[8], r[9], r[10], r[11]), pack_fp8x4(r[12], r[13], r[14], r[15]));
+    } else if (KT == kKeyBF16) {
         uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ckey) + brow * kHeadDim + 16 * e);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -88,12 +93,16 @@ hipError_t launch_compress(const PagedKV& kv, const int32_t* first_token, int sp
     // tokens [first, first + span) touch at most ceil(span / 64) + 1 chunks
     const int chunks = first_token ? (span + 63) / 64 + 1 : (kv.max_seq_len + 63) / 64;
     dim3 grid(chunks, kv.Hkv, kv.batch);
-    if (kv.ckey_bf16)
-        hipLaunchKernelGGL(compress_kernel<true>, grid, dim3(256), 0, st, kv.k, kv.ckey, kv.block_table, kv.seq_lens,
-                           first_token, kv.Hkv, kv.lg_ps, kv.max_pages);
+#define QSA_COMPRESS(KT)                                                                                        \
+    hipLaunchKernelGGL(compress_kernel<KT>, grid, dim3(256), 0, st, kv.k, kv.ckey, kv.block_table, kv.seq_lens, \
+                       first_token, kv.Hkv, kv.lg_ps, kv.max_pages)
+    if (kv.ckey_type == kKeyFP8)
+        QSA_COMPRESS(kKeyFP8);
+    else if (kv.ckey_type == kKeyBF16)
+        QSA_COMPRESS(kKeyBF16);
     else
-        hipLaunchKernelGGL(compress_kernel<false>, grid, dim3(256), 0, st, kv.k, kv.ckey, kv.block_table,
-                           kv.seq_lens, first_token, kv.Hkv, kv.lg_ps, kv.max_pages);
+        QSA_COMPRESS(kKeyF32);
+#undef QSA_COMPRESS
     return hipGetLastError();
 }
 

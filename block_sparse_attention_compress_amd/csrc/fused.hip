@@ -457,7 +457,7 @@ __device__ __forceinline__ void merge_unit(const FusedParams& F, int row, int h)
 
 // ---------------------------------------------------------------- kernel
 
-template <bool PAGE16, bool BF16>
+template <bool PAGE16, int KT>
 __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void fused_decode_kernel(
     const FusedParams F) {
     extern __shared__ float smem[];
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
             if (j >= nch) continue;  // past the row: not counted
             const int wb0 = j * kStreamChunk + wave * (kStreamChunk / 4);
             if (wb0 < n_elig)
-                scan_wave<PAGE16, true, BF16>(F.q + (int64_t)row * F.q_stride + (int64_t)h * F.g * kHeadDim, F.g,
+                scan_wave<PAGE16, true, KT>(F.q + (int64_t)row * F.q_stride + (int64_t)h * F.g * kHeadDim, F.g,
                                         F.ckey, F.block_table + (int64_t)row * F.max_pages, F.Hkv, h, F.lg_ps,
                                         n_elig, wb0, lane, srow);
             // The scores went out as device-scope stores: once every wave has seen
@@ -578,7 +578,7 @@ int fused_capacity(size_t lds) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<true, false>, kFusedThreads, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<true, kKeyF32>, kFusedThreads, lds) !=
         hipSuccess)
         return 0;
     return cus * (per_cu > 0 ? per_cu : 1);
@@ -672,14 +672,23 @@ hipError_t launch_fused_decode(const PagedKV& kv, const Rows& rows, int k, float
     const int resident = cap > 0 ? cap : 512;
     const int grid = F.n_items < resident ? F.n_items : resident;
     const bool page16 = kv.lg_ps >= 6;
-    if (page16 && kv.ckey_bf16)
-        hipLaunchKernelGGL((fused_decode_kernel<true, true>), dim3(grid), dim3(kFusedThreads), lds, st, F);
-    else if (page16)
-        hipLaunchKernelGGL((fused_decode_kernel<true, false>), dim3(grid), dim3(kFusedThreads), lds, st, F);
-    else if (kv.ckey_bf16)
-        hipLaunchKernelGGL((fused_decode_kernel<false, true>), dim3(grid), dim3(kFusedThreads), lds, st, F);
+#define QSA_FUSED(P16, KT) \
+    hipLaunchKernelGGL((fused_decode_kernel<P16, KT>), dim3(grid), dim3(kFusedThreads), lds, st, F)
+#define QSA_FUSED_KT(P16)                  \
+    do {                                   \
+        if (kv.ckey_type == kKeyFP8)       \
+            QSA_FUSED(P16, kKeyFP8);       \
+        else if (kv.ckey_type == kKeyBF16) \
+            QSA_FUSED(P16, kKeyBF16);      \
+        else                               \
+            QSA_FUSED(P16, kKeyF32);       \
+    } while (0)
+    if (page16)
+        QSA_FUSED_KT(true);
     else
-        hipLaunchKernelGGL((fused_decode_kernel<false, false>), dim3(grid), dim3(kFusedThreads), lds, st, F);
+        QSA_FUSED_KT(false);
+#undef QSA_FUSED_KT
+#undef QSA_FUSED
     return hipGetLastError();
 }
 

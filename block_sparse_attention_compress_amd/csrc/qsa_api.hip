@@ -59,8 +59,9 @@ int check_kv(const qsa_kv_t* kv, bool need_k, bool need_v, bool need_ckey, qsa::
     if (kv->num_pages < 1 || kv->max_pages_per_seq < 1)
         return fail(QSA_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be >= 1");
     if (kv->max_seq_len < 0) return fail(QSA_ERR_INVALID_ARG, "max_seq_len %d < 0", kv->max_seq_len);
-    if (kv->ckey_dtype != QSA_CKEY_FP32 && kv->ckey_dtype != QSA_CKEY_BF16)
-        return fail(QSA_ERR_INVALID_ARG, "ckey_dtype %d is neither QSA_CKEY_FP32 nor QSA_CKEY_BF16", kv->ckey_dtype);
+    if (kv->ckey_dtype != QSA_CKEY_FP32 && kv->ckey_dtype != QSA_CKEY_BF16 && kv->ckey_dtype != QSA_CKEY_FP8)
+        return fail(QSA_ERR_INVALID_ARG, "ckey_dtype %d is not QSA_CKEY_FP32, QSA_CKEY_BF16 or QSA_CKEY_FP8",
+                    kv->ckey_dtype);
     if (kv->max_seq_len > QSA_MAX_SEQ_LEN)
         return fail(QSA_ERR_UNSUPPORTED, "max_seq_len %d exceeds %d", kv->max_seq_len, QSA_MAX_SEQ_LEN);
     if ((int64_t)kv->max_pages_per_seq * kv->page_size < kv->max_seq_len)
@@ -71,7 +72,7 @@ int check_kv(const qsa_kv_t* kv, bool need_k, bool need_v, bool need_ckey, qsa::
     out->k = static_cast<const uint16_t*>(kv->k);
     out->v = static_cast<const uint16_t*>(kv->v);
     out->ckey = kv->ckey;
-    out->ckey_bf16 = kv->ckey_dtype == QSA_CKEY_BF16;
+    out->ckey_type = kv->ckey_dtype;  // QSA_CKEY_* values are the kernels' key types
     out->block_table = kv->block_table;
     out->seq_lens = kv->seq_lens;
     out->batch = kv->batch;

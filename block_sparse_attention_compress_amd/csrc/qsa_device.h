@@ -26,6 +26,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Block-key storage types (qsa_kv_t.ckey_dtype).
+constexpr int kKeyF32 = 0;
+constexpr int kKeyBF16 = 1;
+constexpr int kKeyFP8 = 2;  // OCP E4M3 ("fn": bias 7, largest finite 448)
+
+// 4 floats -> 4 E4M3 codes (first value in the low byte), rounded to nearest
+// even by the conversion unit; magnitudes past 448 are held at 448.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+    auto sat = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+    return (uint32_t)w;
+}
+
+// 4 E4M3 codes (low byte first) -> 4 floats (exact).
+__device__ __forceinline__ float4 unpack_fp8x4(uint32_t w) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    return make_float4(lo[0], lo[1], hi[0], hi[1]);
+}
+
 // Block key element: the fp32 mean of the first n (1..4) of a block's keys,
 // ((k0 + k1) + (k2 + k3)) * 0.25 for a full block, the left-to-right sum divided
 // by n (correctly rounded) for a partial last block.

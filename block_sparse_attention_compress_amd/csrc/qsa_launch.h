@@ -11,8 +11,8 @@ namespace qsa {
 struct PagedKV {
     const uint16_t* k;
     const uint16_t* v;
-    void* ckey;               // fp32 or bf16 block keys (ckey_bf16)
-    int ckey_bf16;
+    void* ckey;               // block keys of type ckey_type
+    int ckey_type;            // 0 fp32, 1 bf16, 2 fp8 E4M3 (kKeyF32 / kKeyBF16 / kKeyFP8)
     const int32_t* block_table;
     const int32_t* seq_lens;
     int batch, Hkv, lg_ps, num_pages, max_pages, max_seq_len;

@@ -23,23 +23,28 @@ constexpr int kGroups = kStreamChunk / 64;  // 16-block groups per wave
 // past the row end are still inside the page; their sums are never written).
 // COHERENT: scores are stored at device scope (written through to where every
 // CU reads them), for a reader in another workgroup of the same launch.
-// BF16: block keys are bf16 (8 bytes per lane and block instead of 16); they
-// are kept raw until the dot product, so the next group's loads still fly
-// while a group is reduced.
+// KT: block-key type.  bf16 keys are 8 bytes per lane and block, fp8 E4M3 keys
+// 4 bytes (16 for fp32); they are kept raw until the dot product, so the next
+// group's loads still fly while a group is reduced.
 // REFRESH: the wave named by `rf` first rebuilds one block key from the K cache
 // (the block holding a sequence's newest token), stores it, and scores that
 // block with it in place of the stored, stale key.
-template <bool BF16>
+template <int KT>
 struct KeyRaw {
     typedef float4 type;
     static __device__ __forceinline__ float4 from(const float4& m) { return m; }
 };
 template <>
-struct KeyRaw<true> {
+struct KeyRaw<kKeyBF16> {
     typedef uint2 type;
     static __device__ __forceinline__ uint2 from(const float4& m) {
         return make_uint2(pack_bf16x2(m.x, m.y), pack_bf16x2(m.z, m.w));
     }
+};
+template <>
+struct KeyRaw<kKeyFP8> {
+    typedef uint32_t type;
+    static __device__ __forceinline__ uint32_t from(const float4& m) { return pack_fp8x4(m.x, m.y, m.z, m.w); }
 };
 
 struct Refresh {
@@ -54,12 +59,13 @@ __device__ __forceinline__ float4 key4(const float4& x) { return x; }
 __device__ __forceinline__ float4 key4(const uint2& x) {
     return make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
 }
+__device__ __forceinline__ float4 key4(const uint32_t& x) { return unpack_fp8x4(x); }
 
-template <bool PAGE16, bool COHERENT = false, bool BF16 = false, bool REFRESH = false>
+template <bool PAGE16, bool COHERENT = false, int KT = kKeyF32, bool REFRESH = false>
 __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int g, const void* ckey,
                                           const int32_t* __restrict__ bt, int Hkv, int h, int lg_ps, int n_elig,
                                           int wb0, int lane, float* __restrict__ srow, const Refresh& rf = Refresh{}) {
-    typedef typename KeyRaw<BF16>::type Raw;
+    typedef typename KeyRaw<KT>::type Raw;
     const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
     const int lg_bpp = lg_ps - 2;  // blocks per page = page_size / 4
     // block-key rows of the wave's groups (PAGE16), looked up before any wait
@@ -105,7 +111,7 @@ __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int
         m.y = block_mean(bf16_hi(a[0].x), bf16_hi(a[1].x), bf16_hi(a[2].x), bf16_hi(a[3].x), rf.n);
         m.z = block_mean(bf16_lo(a[0].y), bf16_lo(a[1].y), bf16_lo(a[2].y), bf16_lo(a[3].y), rf.n);
         m.w = block_mean(bf16_hi(a[0].y), bf16_hi(a[1].y), bf16_hi(a[2].y), bf16_hi(a[3].y), rf.n);
-        const Raw fresh = KeyRaw<BF16>::from(m);
+        const Raw fresh = KeyRaw<KT>::from(m);
         // block-key row in [num_pages][Hkv][page_size / 4][256]
         const int64_t brow = ((row >> lg_ps) << (lg_ps - 2)) + ((row & ((1 << lg_ps) - 1)) >> 2);
         reinterpret_cast<Raw*>(rf.ckey)[brow * (kHeadDim / 4) + lane] = fresh;

@@ -22,7 +22,7 @@
 
 namespace qsa {
 
-template <bool PAGE16, bool BF16, bool REFRESH>
+template <bool PAGE16, int KT, bool REFRESH>
 __global__ __launch_bounds__(256) void scores_stream_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int g, const void* ckey, const int32_t* __restrict__ block_table,
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
             rf.stash = stash + wave * 64;
         }
     }
-    scan_wave<PAGE16, false, BF16, REFRESH>(q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim, g, ckey,
+    scan_wave<PAGE16, false, KT, REFRESH>(q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim, g, ckey,
                                             block_table + (int64_t)seq * max_pages, Hkv, h, lg_ps, n_elig, wb0, lane,
                                             scores + ((int64_t)row * Hkv + h) * score_stride, rf);
 }
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
 constexpr int kTiledChunk = 512;
 constexpr int kTRow = kHeadDim + 4;  // padded key row of an LDS tile (floats)
 
-template <bool BF16>
+template <int KT>
 __global__ __launch_bounds__(256) void scores_tiled_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int R, int g, const void* __restrict__ ckey,
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
     float* __restrict__ scores, int score_stride) {
     __shared__ float ktile[2][16 * kTRow];
     __shared__ int w_smin[4], w_smax[4], w_nend[4];
-    typedef typename KeyRaw<BF16>::type Raw;
+    typedef typename KeyRaw<KT>::type Raw;
     const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
     const int h = blockIdx.y;
     const int bc0 = blockIdx.z * kTiledChunk;  // this workgroup's first block
@@ -283,25 +283,31 @@ hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scor
     if (rows.R == 0) return hipSuccess;
     dim3 grid((score_stride + kStreamChunk - 1) / kStreamChunk, kv.Hkv, rows.R);
     const bool page16 = kv.lg_ps >= 6;
-#define QSA_SCAN(P16, B16, RF)                                                                                     \
-    hipLaunchKernelGGL((scores_stream_kernel<P16, B16, RF>), grid, dim3(256), 0, st, rows.q, rows.q_stride,         \
+#define QSA_SCAN(P16, KT, RF)                                                                                      \
+    hipLaunchKernelGGL((scores_stream_kernel<P16, KT, RF>), grid, dim3(256), 0, st, rows.q, rows.q_stride,          \
                        rows.q_seq, rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv,      \
                        kv.lg_ps, kv.max_pages, scores, score_stride, kv.k)
-#define QSA_SCAN_RF(P16, B16)  \
-    do {                       \
-        if (refresh)           \
-            QSA_SCAN(P16, B16, true); \
-        else                   \
-            QSA_SCAN(P16, B16, false); \
+#define QSA_SCAN_RF(P16, KT)          \
+    do {                              \
+        if (refresh)                  \
+            QSA_SCAN(P16, KT, true);  \
+        else                          \
+            QSA_SCAN(P16, KT, false); \
     } while (0)
-    if (page16 && kv.ckey_bf16)
-        QSA_SCAN_RF(true, true);
-    else if (page16)
-        QSA_SCAN_RF(true, false);
-    else if (kv.ckey_bf16)
-        QSA_SCAN_RF(false, true);
+#define QSA_SCAN_KT(P16)                   \
+    do {                                   \
+        if (kv.ckey_type == kKeyFP8)       \
+            QSA_SCAN_RF(P16, kKeyFP8);     \
+        else if (kv.ckey_type == kKeyBF16) \
+            QSA_SCAN_RF(P16, kKeyBF16);    \
+        else                               \
+            QSA_SCAN_RF(P16, kKeyF32);     \
+    } while (0)
+    if (page16)
+        QSA_SCAN_KT(true);
     else
-        QSA_SCAN_RF(false, false);
+        QSA_SCAN_KT(false);
+#undef QSA_SCAN_KT
 #undef QSA_SCAN_RF
 #undef QSA_SCAN
     return hipGetLastError();
@@ -311,14 +317,17 @@ hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* score
                                hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
     dim3 grid((rows.R + 63) / 64, kv.Hkv, (score_stride + kTiledChunk - 1) / kTiledChunk);
-    if (kv.ckey_bf16)
-        hipLaunchKernelGGL(scores_tiled_kernel<true>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,
-                           rows.q_pos, rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv,
-                           kv.lg_ps, kv.max_pages, scores, score_stride);
+#define QSA_TILED(KT)                                                                                            \
+    hipLaunchKernelGGL(scores_tiled_kernel<KT>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,       \
+                       rows.q_pos, rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps, \
+                       kv.max_pages, scores, score_stride)
+    if (kv.ckey_type == kKeyFP8)
+        QSA_TILED(kKeyFP8);
+    else if (kv.ckey_type == kKeyBF16)
+        QSA_TILED(kKeyBF16);
     else
-        hipLaunchKernelGGL(scores_tiled_kernel<false>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,
-                           rows.q_pos, rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv,
-                           kv.lg_ps, kv.max_pages, scores, score_stride);
+        QSA_TILED(kKeyF32);
+#undef QSA_TILED
     return hipGetLastError();
 }
 

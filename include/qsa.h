@@ -60,6 +60,7 @@ extern "C" {
 #define QSA_MAX_SEQ_LEN (1 << 20)   /* tokens per sequence */
 #define QSA_CKEY_FP32 0             /* block keys stored as fp32 */
 #define QSA_CKEY_BF16 1             /* block keys stored as bf16 (rounded fp32 means) */
+#define QSA_CKEY_FP8 2              /* block keys stored as fp8 E4M3 (rounded, saturated fp32 means) */
 
 /*
  * Paged KV cache.  Page p of the pool holds, for every KV head, page_size
@@ -73,7 +74,11 @@ extern "C" {
  *                the fp32 mean below rounded to the nearest bf16, ties to even
  *                (half the bytes of the dominant decode stream; the page on
  *                batch-sharded sampling, section on the surrounding patch
- *                cluster, records smaller cache formats for this path).
+ *                cluster, records smaller cache formats for this path).  With
+ *                QSA_CKEY_FP8 it holds one byte per element: OCP E4M3 ("fn":
+ *                bias 7, 3 mantissa bits, largest finite 448, no infinities),
+ *                the fp32 mean rounded to nearest, ties to the even code, and
+ *                held at +-448 past that range (a quarter of the fp32 bytes).
  *   block_table int32 [batch][max_pages_per_seq]: token i of sequence s lives
  *                in page block_table[s][i / page_size], slot i % page_size.
  *   seq_lens    int32 [batch]: L_s, 0 <= L_s <= max_seq_len.
@@ -84,7 +89,7 @@ extern "C" {
 typedef struct qsa_kv {
     const void* k;
     const void* v;
-    void* ckey;              /* fp32 or bf16 block keys, by ckey_dtype */
+    void* ckey;              /* fp32, bf16 or fp8 block keys, by ckey_dtype */
     const int32_t* block_table;
     const int32_t* seq_lens;
     int32_t batch;
@@ -94,7 +99,7 @@ typedef struct qsa_kv {
     int32_t num_pages;
     int32_t max_pages_per_seq;
     int32_t max_seq_len;
-    int32_t ckey_dtype;      /* QSA_CKEY_FP32 (0) or QSA_CKEY_BF16 */
+    int32_t ckey_dtype;      /* QSA_CKEY_FP32 (0), QSA_CKEY_BF16 (1) or QSA_CKEY_FP8 (2) */
 } qsa_kv_t;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -108,8 +113,8 @@ QSA_API const char* qsa_last_error(void);
  * with 4b < L_s and 4b + 3 >= first_token[s] (first_token NULL = 0), writes
  *   ckey[b] = fp32 mean of the block's n = min(4, L_s - 4b) keys,
  * computed exactly as ((k0 + k1) + (k2 + k3)) * 0.25 for n = 4 and as the
- * left-to-right sum divided by n (correctly rounded) for n < 4 (bf16 block
- * keys: that mean rounded to nearest, ties to even).  The pages
+ * left-to-right sum divided by n (correctly rounded) for n < 4 (bf16 and fp8
+ * block keys: that mean rounded to nearest, ties to even; fp8 held at +-448).  The pages
  * say only that keys are compressed into 4-token microblocks; this pooling is
  * the stated reading.  Idempotent: a page shared by two sequences gets the
  * same values from both.  Decode calls it with first_token = L_s - 1 to

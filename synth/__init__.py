@@ -143,7 +143,7 @@ class Case:
     bias_mag: float = 3.0
     shuffle: bool = True
     shared_prefix_pages: int = 0     # sequence i>0 reuses the first pages of sequence 0
-    ckey_dtype: str = "fp32"         # storage of the block keys: "fp32" or "bf16"
+    ckey_dtype: str = "fp32"         # storage of the block keys: "fp32", "bf16" or "fp8"
     block_table: np.ndarray = field(default=None, repr=False)   # int32 [B][max_pages]
     num_pages: int = 0
     _q: Optional[np.ndarray] = field(default=None, repr=False)
@@ -255,8 +255,8 @@ class Case:
 def to_device(case: Case, device="cuda", ckey: bool = True):
     """Upload a case's paged pool, tables and queries as torch tensors (layout only).
 
-    Returns a dict: k, v (bf16 [num_pages][Hkv][page_size][D]), ckey (fp32 or bf16 as the
-    case stores block keys, zeroed),
+    Returns a dict: k, v (bf16 [num_pages][Hkv][page_size][D]), ckey (fp32, bf16 or fp8
+    E4M3 as the case stores block keys, zeroed),
     block_table, seq_lens, q_seq, q_pos (int32), q (bf16 [R][Hq][D])."""
     import torch
 
@@ -273,7 +273,7 @@ def to_device(case: Case, device="cuda", ckey: bool = True):
         "q": bf16(case.q),
     }
     if ckey:
-        dt = torch.bfloat16 if case.ckey_dtype == "bf16" else torch.float32
+        dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}.get(case.ckey_dtype, torch.float32)
         out["ckey"] = torch.zeros((case.num_pages, case.Hkv, case.page_size // 4, case.D), dtype=dt, device=device)
     return out
 

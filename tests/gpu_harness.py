@@ -80,11 +80,22 @@ class Dev:
         c = self.case
         nb = c.nb(i)
         t = self.t["ckey"]
-        if t.dtype == torch.bfloat16:  # widened to float32 (exact)
+        if t.dtype == torch.float8_e4m3fn:  # decoded to float32 (exact)
+            pool = t.cpu().to(torch.float32).numpy()
+        elif t.dtype == torch.bfloat16:  # widened to float32 (exact)
             pool = synth.bf16_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
         else:
             pool = t.cpu().numpy()
         b = np.arange(nb)
+        pages = c.block_table[i][(4 * b) // c.page_size]
+        slots = ((4 * b) % c.page_size) // 4
+        return np.ascontiguousarray(pool[pages, :, slots, :].transpose(1, 0, 2))
+
+    def ckey_codes(self, i: int) -> np.ndarray:
+        """fp8 block-key codes of sequence i as uint8 [Hkv][nb][256]."""
+        c = self.case
+        b = np.arange(c.nb(i))
+        pool = self.t["ckey"].view(torch.uint8).cpu().numpy()
         pages = c.block_table[i][(4 * b) // c.page_size]
         slots = ((4 * b) % c.page_size) // 4
         return np.ascontiguousarray(pool[pages, :, slots, :].transpose(1, 0, 2))

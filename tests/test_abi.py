@@ -50,6 +50,7 @@ def test_header_constants_match_binding():
     assert int(consts["QSA_ERR_INVALID_ARG"]) == qsa.QSA_ERR_INVALID_ARG
     assert int(consts["QSA_CKEY_FP32"]) == qsa.CKEY_FP32 == 0
     assert int(consts["QSA_CKEY_BF16"]) == qsa.CKEY_BF16
+    assert int(consts["QSA_CKEY_FP8"]) == qsa.CKEY_FP8 == 2
 
 
 @pytest.mark.parametrize("over,code", [
@@ -64,7 +65,7 @@ def test_header_constants_match_binding():
     (dict(num_pages=1 << 24), qsa.QSA_ERR_UNSUPPORTED),          # 2^24 pages x 2 heads x 64 rows = 2^31
     (dict(k=P + 8), qsa.QSA_ERR_INVALID_ARG),                    # misaligned
     (dict(batch=-1), qsa.QSA_ERR_INVALID_ARG),
-    (dict(ckey_dtype=2), qsa.QSA_ERR_INVALID_ARG),
+    (dict(ckey_dtype=3), qsa.QSA_ERR_INVALID_ARG),
     (dict(ckey_dtype=-1), qsa.QSA_ERR_INVALID_ARG),
 ])
 def test_compress_rejects(over, code):

@@ -62,7 +62,7 @@ def both_paths(case, stride=None, drop_host=False):
     return d, s1
 
 
-@pytest.mark.parametrize("ckey_dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("ckey_dtype", ["fp32", "bf16", "fp8"])
 @pytest.mark.parametrize("page_size,lens", [
     (64, [4096, 4097, 4098, 4099, 1, 5]),   # L mod 4 = 0..3; one- and two-block rows
     (4, [37, 64, 1, 2]),
