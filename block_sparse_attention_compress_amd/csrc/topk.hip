@@ -74,12 +74,10 @@ __device__ __forceinline__ int eligible(const int32_t* q_pos, int row, int score
 
 // ------------------------------------------------------------------ registers
 
-constexpr int kRegThreads = 1024;
-constexpr int kRegWaves = kRegThreads / 64;
+constexpr int kRegThreads = 1024;  // threads per row, unless many rows share the launch
+constexpr int kManyThreads = 256;  // threads per row when rows are many (extend chunks)
 constexpr int kBins = 2048;
 
-// KPT scores per thread: the first KR in registers, the rest in LDS (a 65,536-block
-// row would not fit 1024 threads x 128 registers).
 // Candidate workspace of the two-stage select for long rows: per (row, KV head),
 // nslices x k (value, block index) pairs, slice j's top k in ascending index order.
 struct SplitWs {
@@ -89,20 +87,25 @@ struct SplitWs {
     int nslices;  // ceil(score_stride / slice)
 };
 
-template <int KPT, int KR, int MODE>
-__global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __restrict__ scores, int score_stride,
-                                                               const int32_t* __restrict__ q_pos, int Hkv, int k,
-                                                               int32_t* __restrict__ sel_idx,
-                                                               int32_t* __restrict__ sel_cnt, SplitWs ws) {
+// NT threads per row, KPT scores per thread: the first KR in registers, the rest
+// in LDS (a 65,536-block row would not fit 1024 threads x 128 registers).  Thread
+// t owns histogram bins [BPT t, BPT t + BPT).
+template <int NT, int KPT, int KR, int MODE>
+__global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ scores, int score_stride,
+                                                      const int32_t* __restrict__ q_pos, int Hkv, int k,
+                                                      int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
+                                                      SplitWs ws) {
+    constexpr int NW = NT / 64;
+    constexpr int BPT = kBins / NT;
     __shared__ int hist[kBins];
-    __shared__ float cand_val[kRegThreads];
-    __shared__ int cand_idx[kRegThreads];
-    __shared__ int itmp[2 * kRegWaves];
+    __shared__ float cand_val[NT];
+    __shared__ int cand_idx[NT];
+    __shared__ int itmp[2 * NW];
     __shared__ float ftmp[64];
     __shared__ int sh_bin, sh_above, sh_ncand, sh_need_eq, sh_m;
     __shared__ uint32_t sh_T;
     constexpr int KL = KPT - KR;
-    __shared__ float vl[KL > 0 ? KL * kRegThreads : 1];
+    __shared__ float vl[KL > 0 ? KL * NT : 1];
 
     const int unit = blockIdx.x;
     const int n_row = eligible(q_pos, unit / Hkv, score_stride);
@@ -157,14 +160,14 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     const int tid = threadIdx.x;
     const int i0 = tid * KPT;  // this thread's first block
     // the histogram is cleared while the loads fly; block_min_max's barrier orders it
-    for (int i = tid; i < kBins; i += kRegThreads) hist[i] = 0;
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
     // slots past n hold -inf (scores are finite): it is never selected, and
     // every test below stays a function of the value (no per-slot masks kept live)
     float v[KR];
     auto put = [&](int e, float raw) {
         const float x = i0 + e < n ? raw + 0.0f : -INFINITY;  // + 0 turns -0 into +0
         if (e < KR) v[e < KR ? e : 0] = x;
-        else vl[(e - KR) * kRegThreads + tid] = x;
+        else vl[(e - KR) * NT + tid] = x;
     };
     if (KPT >= 4 && (row_len & 3) == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
         // float4 loads, clamped and unconditional, so all KPT / 4 are in flight at once
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
 #pragma unroll
         for (int e = 0; e < KPT; ++e) put(e, s[min(i0 + e, n - 1)]);
     }
-    auto V = [&](int e) -> float { return e < KR ? v[e < KR ? e : 0] : vl[(e - KR) * kRegThreads + tid]; };
+    auto V = [&](int e) -> float { return e < KR ? v[e < KR ? e : 0] : vl[(e - KR) * NT + tid]; };
     float mn = FLT_MAX, mx = -FLT_MAX;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     }
     const float range = block_min_max(mn, mx, ftmp);
     if (range == 0.f) {  // every score equal: the k lowest indices (positions are in index order)
-        for (int j = tid; j < k; j += kRegThreads) emit(j, j, mn);
+        for (int j = tid; j < k; j += NT) emit(j, j, mn);
         if (tid == 0 && final_out) sel_cnt[unit] = k;
         return;
     }
@@ -206,31 +209,39 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
     for (int e = 0; e < KPT; ++e)
         if (V(e) != -INFINITY) atomicAdd(&hist[bin_of(V(e))], 1);
     __syncthreads();
-    {
-        const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
-        const int incl = block_suffix_sum<kRegWaves, false>(h0 + h1, itmp);
-        const int above = incl - h0 - h1;
-        if (above < k && k <= incl) {
-            if (above + h1 >= k) {
-                sh_bin = 2 * tid + 1;
-                sh_above = above;
-                sh_m = h1;
-            } else {
-                sh_bin = 2 * tid;
-                sh_above = above + h1;
-                sh_m = h0;
+    // the thread whose bins hold the k-th largest names the bin (bins descend with
+    // the score from the top one down)
+    auto find_bin = [&](int want, bool keep_m) {
+        int hb[BPT], local = 0;
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) {
+            hb[b] = hist[BPT * tid + b];
+            local += hb[b];
+        }
+        const int incl = block_suffix_sum<NW, false>(local, itmp);
+        int cum = incl - local;  // elements in higher bins
+        if (cum < want && want <= incl) {
+#pragma unroll
+            for (int b = BPT - 1; b >= 0; --b) {
+                if (cum < want && cum + hb[b] >= want) {
+                    sh_bin = BPT * tid + b;
+                    sh_above = cum;
+                    if (keep_m) sh_m = hb[b];
+                }
+                cum += hb[b];
             }
         }
-        if (tid == 0) sh_ncand = 0;
-        __syncthreads();
-    }
+    };
+    find_bin(k, true);
+    if (tid == 0) sh_ncand = 0;
+    __syncthreads();
     const int B = sh_bin;
     const int need = k - sh_above;  // how many of bin B's elements are taken (>= 1)
     // bin B's size, from a copy: the crowded path below clears hist with no barrier
     // between this read and the clear
     const int m = sh_m;
 
-    if (m <= kRegThreads) {
+    if (m <= NT) {
         // ---- rank the bin's candidates directly
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
         for (int pass = 0; pass < 3; ++pass) {
             const int shift = shifts[pass];
             const int nb = 1 << widths[pass];
-            for (int i = tid; i < kBins; i += kRegThreads) hist[i] = 0;
+            for (int i = tid; i < kBins; i += NT) hist[i] = 0;
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
@@ -274,18 +285,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
                     atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
             }
             __syncthreads();
-            const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
-            const int incl = block_suffix_sum<kRegWaves, false>(h0 + h1, itmp);
-            const int above = incl - h0 - h1;
-            if (above < remaining && remaining <= incl) {
-                if (above + h1 >= remaining) {
-                    sh_bin = 2 * tid + 1;
-                    sh_above = above;
-                } else {
-                    sh_bin = 2 * tid;
-                    sh_above = above + h1;
-                }
-            }
+            find_bin(remaining, false);
             __syncthreads();
             remaining -= sh_above;
             prefix |= (uint32_t)sh_bin << shift;
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
         gt += real && key > T;
         eq += real && key == T;
     }
-    block_exclusive_scan2<kRegWaves, false>(gt, eq, itmp);  // last use of itmp
+    block_exclusive_scan2<NW, false>(gt, eq, itmp);  // last use of itmp
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         if (V(e) == -INFINITY) continue;
@@ -427,12 +427,12 @@ __global__ __launch_bounds__(kGlobThreads) void topk_global_kernel(const float* 
     if (tid == 0) sel_cnt[unit] = k;
 }
 
-template <int MODE>
+template <int MODE, int NT = kRegThreads>
 static void launch_reg(int per, dim3 grid, const float* scores, int score_stride, const int32_t* q_pos, int Hkv, int k,
                        int32_t* sel_idx, int32_t* sel_cnt, SplitWs ws, hipStream_t st) {
-#define QSA_TOPK_REG(KPT, KR)                                                                                  \
-    hipLaunchKernelGGL((topk_reg_kernel<KPT, KR, MODE>), grid, dim3(kRegThreads), 0, st, scores, score_stride, \
-                       q_pos, Hkv, k, sel_idx, sel_cnt, ws)
+#define QSA_TOPK_REG(KPT, KR)                                                                                   \
+    hipLaunchKernelGGL((topk_reg_kernel<NT, KPT, KR, MODE>), grid, dim3(NT), 0, st, scores, score_stride, q_pos, \
+                       Hkv, k, sel_idx, sel_cnt, ws)
     if (per <= 1) QSA_TOPK_REG(1, 1);
     else if (per <= 2) QSA_TOPK_REG(2, 2);
     else if (per <= 4) QSA_TOPK_REG(4, 4);
@@ -443,12 +443,20 @@ static void launch_reg(int per, dim3 grid, const float* scores, int score_stride
 #undef QSA_TOPK_REG
 }
 
+// With many rows per launch (an extend chunk), 256-thread workgroups let 8 rows
+// share a CU and hide each other's latency; with few, 1024 threads shorten each row.
+constexpr int kManyRows = 1024;
+
 hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,
                        int32_t* sel_idx, int32_t* sel_cnt, hipStream_t st) {
     if (R == 0) return hipSuccess;
     const int units = R * Hkv;
     const int per = (score_stride + kRegThreads - 1) / kRegThreads;  // scores per thread
-    if (per <= 64)
+    const int per_many = (score_stride + kManyThreads - 1) / kManyThreads;
+    if (units >= kManyRows && per_many <= 64)
+        launch_reg<0, kManyThreads>(per_many, dim3(units), scores, score_stride, q_pos, Hkv, k, sel_idx, sel_cnt,
+                                    SplitWs{}, st);
+    else if (per <= 64)
         launch_reg<0>(per, dim3(units), scores, score_stride, q_pos, Hkv, k, sel_idx, sel_cnt, SplitWs{}, st);
     else
         hipLaunchKernelGGL(topk_global_kernel, dim3(units), dim3(kGlobThreads), 0, st, scores, score_stride, q_pos,

@@ -125,3 +125,22 @@ def test_workspace_reused_by_a_smaller_call():
     ws = torch.empty(qsa.qsa_topk_workspace_bytes(4, 2, 512, 70000), dtype=torch.uint8, device="cuda")
     for sc in (big, small, big):
         check(sc, None, 512, ws=ws)
+
+
+def test_many_rows_use_the_256_thread_kernel_bit_exact():
+    """1,100 rows of one KV head: the launch takes 256 threads per row.  Random,
+    heavily tied (bins crowded past 256 candidates: the radix passes), all-equal
+    and short rows, with eligibility from q_pos, against the oracle."""
+    rng = np.random.default_rng(23)
+    R, stride = 1100, 5000
+    s = (rng.standard_normal((R, 1, stride)) * 20).astype(np.float32)
+    s[100:200] = rng.integers(-3, 4, size=(100, 1, stride)).astype(np.float32)
+    s[200:210] = 1.5
+    s[210:220, 0, ::2] = -0.0
+    s[210:220, 0, 1::2] = 0.0
+    q_pos = np.full(R, 4 * stride - 1, dtype=np.int32)
+    q_pos[300:400] = rng.integers(-1, 4 * stride, size=100)
+    q_pos[400:410] = [0, 3, 4, 2043, 2047, 2048, 2051, 7, 11, 15]
+    for k in (512, 37):
+        log(f"topk many rows k={k}")
+        check(s, q_pos, k)
