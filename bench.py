@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--no-fused", action="store_true", help="skip the single-launch fused step figures")
     p.add_argument("--flush", action="store_true",
                    help="also time single steps after a 1 GiB read that evicts the caches (MALL included)")
+    p.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                   help="main cache storage (bf16; fp8: E4M3 codes of the same draws)")
     p.add_argument("--ckey", choices=["fp32", "bf16", "fp8"], default="fp32",
                    help="block-key storage (fp32: the method's definition; bf16 / fp8: the rounded-mean variants)")
     return p.parse_args()
@@ -70,9 +72,9 @@ def describe(case) -> str:
     lo, hi = int(case.lens.min()), int(case.lens.max())
     lens = f"length {lo}" if lo == hi else f"lengths {lo}..{hi} {LENGTH_RANGE.get(case.name, '')}".rstrip()
     if case.block_table.shape[1] == 1:
-        cache = "contiguous bf16 KV"
+        cache = f"contiguous {case.kv_dtype} KV"
     else:
-        cache = f"bf16 paged KV ({case.page_size}-token pages{', shuffled' if case.shuffle else ''})"
+        cache = f"{case.kv_dtype} paged KV ({case.page_size}-token pages{', shuffled' if case.shuffle else ''})"
     extra = []
     if case.jitter:
         extra.append("per-token key/value norm jitter x U(0.5, 2)")
@@ -84,6 +86,8 @@ def describe(case) -> str:
         extra.append("bf16 block keys (fp32 means rounded to nearest even)")
     if case.ckey_dtype == "fp8":
         extra.append("fp8 E4M3 block keys (fp32 means rounded to nearest even, held at +-448)")
+    if case.kv_dtype == "fp8":
+        extra.append("fp8 E4M3 main K/V cache (codes of the bf16 draws, unit scale)")
     return (f"{case.name}: decode, {case.B} sequence{'s' if case.B > 1 else ''}, {lens}, ({case.Hq},{case.Hkv}) heads, "
             f"head_dim 256, {cache}, top-{case.topk} microblocks of 4" + "".join("; " + e for e in extra))
 
@@ -124,7 +128,8 @@ def decode_bytes(case, sel, cnt, page_size):
     nb = np.array([case.nb(i) for i in range(B)], dtype=np.int64)
     key_bytes = 256 * {"bf16": 2, "fp8": 1}.get(case.ckey_dtype, 4)
     ckey = int(nb.sum()) * Hkv * key_bytes
-    refresh = sum((int(L) - 4 * ((int(L) - 1) // 4)) * 512 + key_bytes for L in case.lens if L > 0) * Hkv
+    row_bytes = 256 if case.kv_dtype == "fp8" else 512  # one K or V row
+    refresh = sum((int(L) - 4 * ((int(L) - 1) // 4)) * row_bytes + key_bytes for L in case.lens if L > 0) * Hkv
     tokens = 0
     for i in range(B):
         L = int(case.lens[i])
@@ -132,7 +137,7 @@ def decode_bytes(case, sel, cnt, page_size):
             c = int(cnt[i, h])
             blocks = sel[i, h, :c].astype(np.int64)
             tokens += int(np.minimum(L - 4 * blocks, 4).sum())
-    kv_bytes = tokens * 256 * 2 * 2
+    kv_bytes = tokens * row_bytes * 2
     qo = B * Hq * 256 * 2 * 2 + B * Hq * 4
     table = int(sum((int(L) + page_size - 1) // page_size for L in case.lens)) * 4 + B * 4
     step = ckey + refresh + kv_bytes + qo + table
@@ -182,7 +187,7 @@ def cpu_baseline(case, target_s: float):
             "cpu_model": cpu_model()}
 
 
-def extend_figures(steps: int, flush: bool = False):
+def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv_dtype: str = "bf16"):
     """Extend chunk: 4096 new query tokens on 28672 cached (32768 total), (12, 1) heads."""
     import torch
 
@@ -191,6 +196,7 @@ def extend_figures(steps: int, flush: bool = False):
     from block_sparse_attention_compress_amd.pipeline import ExtendBuffers, extend_step
 
     case = synth.config("C4")
+    case.ckey_dtype, case.kv_dtype = ckey_dtype, kv_dtype
     dev = synth.to_device(case, "cuda")
     kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
     first = torch.tensor([int(case.q_pos[0])], dtype=torch.int32, device="cuda")
@@ -225,7 +231,8 @@ def extend_figures(steps: int, flush: bool = False):
     elig = sum(min(int(t) // 4 + 1, stride) for t in case.q_pos)
     cnt = buf.sel_cnt.cpu().numpy()
     flops = 2 * 256 * elig + 4 * 256 * case.Hq * int(cnt.sum()) * 4
-    return {"workload": "extend: 4096 new tokens on 28672 cached, (12,1) heads, top-512 per query",
+    return {"workload": f"extend: 4096 new tokens on 28672 cached, (12,1) heads, top-512 per query, "
+                        f"{kv_dtype} K/V, {ckey_dtype} block keys",
             "new_tokens_per_s": round(case.R / dt, 1), "ms_per_chunk": round(dt * 1e3, 4),
             "tflops": round(flops / dt / 1e12, 2), "cold_cache_ms_per_chunk_median": cold}
 
@@ -251,6 +258,7 @@ def main():
     qsa.lib()
     case = synth.config(args.config)
     case.ckey_dtype = args.ckey
+    case.kv_dtype = args.kv
     log(f"workload {case.name}: B={case.B} lens {int(case.lens.min())}..{int(case.lens.max())} "
         f"heads ({case.Hq},{case.Hkv}) page {case.page_size}")
     t0 = time.perf_counter()
@@ -373,7 +381,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
         if (rec.get("source_sha256_16") == source_hash(SCORES_SRC) and rec.get("workload") == case.name
-                and rec.get("ckey_dtype", "fp32") == case.ckey_dtype):
+                and rec.get("ckey_dtype", "fp32") == case.ckey_dtype and rec.get("kv_dtype", "bf16") == case.kv_dtype):
             traffic = rec.get("hbm_bytes_per_launch")
 
     result = {
@@ -405,7 +413,7 @@ def main():
                  "full_block_key_build_ms": round(compress_full_ms, 4)},
     }
     if not args.no_extend:
-        result["extend"] = extend_figures(max(3, args.steps // 4), args.flush)
+        result["extend"] = extend_figures(max(3, args.steps // 4), args.flush, args.ckey, args.kv)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -36,6 +36,8 @@ MAX_SPLITS = 64
 CKEY_FP32 = 0
 CKEY_BF16 = 1
 CKEY_FP8 = 2
+KV_BF16 = 0
+KV_FP8 = 1
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks",
            "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse",
@@ -64,6 +66,7 @@ class qsa_kv_t(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int32),
         ("ckey_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
     ]
 
 
@@ -145,9 +148,10 @@ class KVCache:
         num_pages, hkv, page_size, d = self.k.shape
         dt = str(getattr(self.ckey, "dtype", "")) if self.ckey is not None else ""
         ckey_dtype = {"torch.bfloat16": CKEY_BF16, "torch.float8_e4m3fn": CKEY_FP8}.get(dt, CKEY_FP32)
+        kv_dtype = KV_FP8 if str(getattr(self.k, "dtype", "")) == "torch.float8_e4m3fn" else KV_BF16
         return qsa_kv_t(_ptr(self.k), _ptr(self.v), _ptr(self.ckey), _ptr(self.block_table), _ptr(self.seq_lens),
                         int(self.block_table.shape[0]), int(hkv), int(d), int(page_size), int(num_pages),
-                        int(self.block_table.shape[1]), int(self.max_seq_len), ckey_dtype)
+                        int(self.block_table.shape[1]), int(self.max_seq_len), ckey_dtype, kv_dtype)
 
 
 def _kv(kv) -> qsa_kv_t:

@@ -35,11 +35,12 @@
 
 namespace qsa {
 
+template <bool KV8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(const AttnParams P) {
     extern __shared__ float smem[];
     const int unit = blockIdx.x;
     const int uh = unit / P.S;
-    attend_split(P, uh / P.Hkv, uh % P.Hkv, unit % P.S, smem);
+    attend_split<KV8>(P, uh / P.Hkv, uh % P.Hkv, unit % P.S, smem);
 }
 
 hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt, int k,
@@ -77,7 +78,10 @@ hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_i
     const size_t loop = (size_t)P.table_words * 4 + (size_t)kAttnWaves * 2 * kKTile * sizeof(uint16_t);
     const size_t xchg = (size_t)kAttnWaves * P.g * kHeadDim * sizeof(float);
     const size_t lds = loop > xchg ? loop : xchg;
-    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)nblocks), dim3(256), lds, st, P);
+    if (kv.kv_fp8)
+        hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)nblocks), dim3(256), lds, st, P);
+    else
+        hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)nblocks), dim3(256), lds, st, P);
     return hipGetLastError();
 }
 

@@ -45,12 +45,32 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& a, int w) {
     return w == 0 ? a.x : (w == 1 ? a.y : (w == 2 ? a.z : a.w));
 }
 
+// Raw K / V tile registers: 8 bf16 (or 8 fp8 E4M3 codes) of one row per lane.
+template <bool KV8>
+struct KVRaw {
+    typedef uint4 type;
+};
+template <>
+struct KVRaw<true> {
+    typedef uint2 type;
+};
+
+// 8 elements as bf16: fp8 codes are widened exactly (an E4M3 value has at most 4
+// significant bits, so the top half of its fp32 form is its bf16 form).
+__device__ __forceinline__ uint4 kv_bf16x8(const uint4& x) { return x; }
+__device__ __forceinline__ uint4 kv_bf16x8(const uint2& x) {
+    const float4 a = unpack_fp8x4(x.x), b = unpack_fp8x4(x.y);
+    auto pair = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u); };
+    return make_uint4(pair(a.x, a.y), pair(a.z, a.w), pair(b.x, b.y), pair(b.z, b.w));
+}
+
 // LDS: `smem` is dynamic shared memory of the launch: the slot table (16 B per
 // selected block of this work unit, P.table_words int32) and the 4 waves' K and V
 // staging tiles, later reused for the waves' O exchange (4 waves x g heads x
 // 1 KiB); the launch sizes it to the larger need.  Ends with a barrier-free
 // write of the result; the caller separates work units sharing `smem` with a
 // barrier.
+template <bool KV8>
 __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h, int s, float* smem) {
     __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16], h_inv[16], h_lse[16];
     int32_t* slot_row = reinterpret_cast<int32_t*>(smem);
@@ -143,14 +163,22 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
     // computed, so a wave always has a tile in flight.
     // (the raw tile is 16 named registers, not an array: an array indexed in a
     // loop across the tile pipeline was kept in scratch memory)
-    uint4 k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+    // (fp8 rows are 256 bytes: each lane reads 8 codes and widens them to bf16 as
+    // they are staged, so the tiles and everything after them are the same)
+    typedef typename KVRaw<KV8>::type Raw;
+    Raw k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
 #define QSA_LOAD_J(J, KX, VX)                                                               \
     do {                                                                                    \
         const int nr = n0_ + 2 * (J) + (lane >> 5);                                         \
         const int rr = nr < n_s ? slot_row[slot0 + sstep * nr] : -1;                        \
         const int64_t off = (int64_t)max(rr, 0) * kHeadDim + 8 * (lane & 31);               \
-        KX = *reinterpret_cast<const uint4*>(P.k + off);                                    \
-        VX = *reinterpret_cast<const uint4*>(P.v + off);                                    \
+        if (KV8) {                                                                          \
+            KX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.k) + off); \
+            VX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.v) + off); \
+        } else {                                                                            \
+            KX = *reinterpret_cast<const Raw*>(P.k + off);                                  \
+            VX = *reinterpret_cast<const Raw*>(P.v + off);                                  \
+        }                                                                                   \
     } while (0)
 #define QSA_LOAD_RAW(TILE, RV)                                                              \
     do {                                                                                    \
@@ -172,8 +200,8 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
 #define QSA_STAGE_J(J, KX, VX)                                                              \
     do {                                                                                    \
         const int r = 2 * (J) + (lane >> 5);                                                \
-        *reinterpret_cast<uint4*>(ktile + r * kKRow + 8 * (lane & 31)) = KX;                \
-        *reinterpret_cast<uint4*>(vtile + r * kKRow + 8 * (lane & 31)) = VX;                \
+        *reinterpret_cast<uint4*>(ktile + r * kKRow + 8 * (lane & 31)) = kv_bf16x8(KX);     \
+        *reinterpret_cast<uint4*>(vtile + r * kKRow + 8 * (lane & 31)) = kv_bf16x8(VX);     \
     } while (0)
     int rv_cur[4], rv_nxt[4];
     QSA_LOAD_RAW(wave, rv_cur);

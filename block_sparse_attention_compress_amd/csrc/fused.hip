@@ -457,7 +457,7 @@ __device__ __forceinline__ void merge_unit(const FusedParams& F, int row, int h)
 
 // ---------------------------------------------------------------- kernel
 
-template <bool PAGE16, int KT>
+template <bool PAGE16, int KT, bool KV8>
 __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void fused_decode_kernel(
     const FusedParams F) {
     extern __shared__ float smem[];
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
-            attend_split(F.A, row, h, j, smem);
+            attend_split<KV8>(F.A, row, h, j, smem);
             __syncthreads();
             if (tid == 0) {
                 const bool last = __hip_atomic_fetch_add(&F.att_arrive[u], 1, __ATOMIC_RELEASE,
@@ -578,7 +578,7 @@ int fused_capacity(size_t lds) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<true, kKeyF32>, kFusedThreads, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<true, kKeyF32, false>, kFusedThreads, lds) !=
         hipSuccess)
         return 0;
     return cus * (per_cu > 0 ? per_cu : 1);
@@ -672,8 +672,13 @@ hipError_t launch_fused_decode(const PagedKV& kv, const Rows& rows, int k, float
     const int resident = cap > 0 ? cap : 512;
     const int grid = F.n_items < resident ? F.n_items : resident;
     const bool page16 = kv.lg_ps >= 6;
-#define QSA_FUSED(P16, KT) \
-    hipLaunchKernelGGL((fused_decode_kernel<P16, KT>), dim3(grid), dim3(kFusedThreads), lds, st, F)
+#define QSA_FUSED(P16, KT)                                                                                      \
+    do {                                                                                                        \
+        if (kv.kv_fp8)                                                                                          \
+            hipLaunchKernelGGL((fused_decode_kernel<P16, KT, true>), dim3(grid), dim3(kFusedThreads), lds, st, F); \
+        else                                                                                                    \
+            hipLaunchKernelGGL((fused_decode_kernel<P16, KT, false>), dim3(grid), dim3(kFusedThreads), lds, st, F); \
+    } while (0)
 #define QSA_FUSED_KT(P16)                  \
     do {                                   \
         if (kv.ckey_type == kKeyFP8)       \

@@ -62,6 +62,8 @@ int check_kv(const qsa_kv_t* kv, bool need_k, bool need_v, bool need_ckey, qsa::
     if (kv->ckey_dtype != QSA_CKEY_FP32 && kv->ckey_dtype != QSA_CKEY_BF16 && kv->ckey_dtype != QSA_CKEY_FP8)
         return fail(QSA_ERR_INVALID_ARG, "ckey_dtype %d is not QSA_CKEY_FP32, QSA_CKEY_BF16 or QSA_CKEY_FP8",
                     kv->ckey_dtype);
+    if (kv->kv_dtype != QSA_KV_BF16 && kv->kv_dtype != QSA_KV_FP8)
+        return fail(QSA_ERR_INVALID_ARG, "kv_dtype %d is neither QSA_KV_BF16 nor QSA_KV_FP8", kv->kv_dtype);
     if (kv->max_seq_len > QSA_MAX_SEQ_LEN)
         return fail(QSA_ERR_UNSUPPORTED, "max_seq_len %d exceeds %d", kv->max_seq_len, QSA_MAX_SEQ_LEN);
     if ((int64_t)kv->max_pages_per_seq * kv->page_size < kv->max_seq_len)
@@ -73,6 +75,7 @@ int check_kv(const qsa_kv_t* kv, bool need_k, bool need_v, bool need_ckey, qsa::
     out->v = static_cast<const uint16_t*>(kv->v);
     out->ckey = kv->ckey;
     out->ckey_type = kv->ckey_dtype;  // QSA_CKEY_* values are the kernels' key types
+    out->kv_fp8 = kv->kv_dtype == QSA_KV_FP8;
     out->block_table = kv->block_table;
     out->seq_lens = kv->seq_lens;
     out->batch = kv->batch;

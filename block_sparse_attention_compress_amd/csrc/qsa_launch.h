@@ -9,8 +9,9 @@
 namespace qsa {
 
 struct PagedKV {
-    const uint16_t* k;
+    const uint16_t* k;        // bf16 rows, or fp8 E4M3 rows when kv_fp8 (the same address)
     const uint16_t* v;
+    int kv_fp8;               // K and V hold fp8 E4M3 codes (256 B per row) instead of bf16
     void* ckey;               // block keys of type ckey_type
     int ckey_type;            // 0 fp32, 1 bf16, 2 fp8 E4M3 (kKeyF32 / kKeyBF16 / kKeyFP8)
     const int32_t* block_table;

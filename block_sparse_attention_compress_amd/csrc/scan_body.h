@@ -48,7 +48,8 @@ struct KeyRaw<kKeyFP8> {
 };
 
 struct Refresh {
-    const uint16_t* k = nullptr;  // K cache [num_pages][Hkv][page_size][256]
+    const void* k = nullptr;      // K cache [num_pages][Hkv][page_size][256], bf16 or fp8 E4M3 (kv8)
+    bool kv8 = false;
     void* ckey = nullptr;         // block keys, written
     int b = -1;                   // block to rebuild (-1: none in this wave)
     int n = 0;                    // its tokens, 1..4
@@ -102,15 +103,27 @@ __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int
         // the block's tokens are consecutive rows of one page; lane: dims 4 lane .. 4 lane + 3
         const int64_t pos0 = 4 * (int64_t)rf.b;
         const int64_t row = (((int64_t)bt[pos0 >> lg_ps] * Hkv + h) << lg_ps) + (pos0 & ((1 << lg_ps) - 1));
-        const uint2* src = reinterpret_cast<const uint2*>(rf.k + row * kHeadDim) + lane;
-        uint2 a[4];
+        float4 kt[4];  // the lane's 4 dims of each token, exact
+        if (rf.kv8) {
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(rf.k) + row * kHeadDim) + lane;
+            uint32_t a[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = u < rf.n ? src[u * (kHeadDim / 4)] : make_uint2(0, 0);
+            for (int u = 0; u < 4; ++u) a[u] = u < rf.n ? src[u * (kHeadDim / 4)] : 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kt[u] = unpack_fp8x4(a[u]);
+        } else {
+            const uint2* src = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(rf.k) + row * kHeadDim) + lane;
+            uint2 a[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a[u] = u < rf.n ? src[u * (kHeadDim / 4)] : make_uint2(0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kt[u] = make_float4(bf16_lo(a[u].x), bf16_hi(a[u].x), bf16_lo(a[u].y), bf16_hi(a[u].y));
+        }
         float4 m;
-        m.x = block_mean(bf16_lo(a[0].x), bf16_lo(a[1].x), bf16_lo(a[2].x), bf16_lo(a[3].x), rf.n);
-        m.y = block_mean(bf16_hi(a[0].x), bf16_hi(a[1].x), bf16_hi(a[2].x), bf16_hi(a[3].x), rf.n);
-        m.z = block_mean(bf16_lo(a[0].y), bf16_lo(a[1].y), bf16_lo(a[2].y), bf16_lo(a[3].y), rf.n);
-        m.w = block_mean(bf16_hi(a[0].y), bf16_hi(a[1].y), bf16_hi(a[2].y), bf16_hi(a[3].y), rf.n);
+        m.x = block_mean(kt[0].x, kt[1].x, kt[2].x, kt[3].x, rf.n);
+        m.y = block_mean(kt[0].y, kt[1].y, kt[2].y, kt[3].y, rf.n);
+        m.z = block_mean(kt[0].z, kt[1].z, kt[2].z, kt[3].z, rf.n);
+        m.w = block_mean(kt[0].w, kt[1].w, kt[2].w, kt[3].w, rf.n);
         const Raw fresh = KeyRaw<KT>::from(m);
         // block-key row in [num_pages][Hkv][page_size / 4][256]
         const int64_t brow = ((row >> lg_ps) << (lg_ps - 2)) + ((row & ((1 << lg_ps) - 1)) >> 2);

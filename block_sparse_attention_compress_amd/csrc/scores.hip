@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int g, const void* ckey, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages, float* __restrict__ scores,
-    int score_stride, const uint16_t* __restrict__ kcache) {
+    int score_stride, const void* __restrict__ kcache, int kv8) {
     const int row = blockIdx.z;
     const int h = blockIdx.y;
     const int seq = q_seq ? q_seq[row] : row;
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
         const bool scored = b < n_elig;
         if (scored ? (wb0 <= b && b < wb0 + kStreamChunk / 4) : wb0 == 0) {
             rf.k = kcache;
+            rf.kv8 = kv8 != 0;
             rf.ckey = const_cast<void*>(ckey);
             rf.b = b;
             rf.n = L - 4 * b;
@@ -286,7 +287,7 @@ hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scor
 #define QSA_SCAN(P16, KT, RF)                                                                                      \
     hipLaunchKernelGGL((scores_stream_kernel<P16, KT, RF>), grid, dim3(256), 0, st, rows.q, rows.q_stride,          \
                        rows.q_seq, rows.q_pos, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv,      \
-                       kv.lg_ps, kv.max_pages, scores, score_stride, kv.k)
+                       kv.lg_ps, kv.max_pages, scores, score_stride, kv.k, kv.kv_fp8)
 #define QSA_SCAN_RF(P16, KT)          \
     do {                              \
         if (refresh)                  \

@@ -61,11 +61,20 @@ extern "C" {
 #define QSA_CKEY_FP32 0             /* block keys stored as fp32 */
 #define QSA_CKEY_BF16 1             /* block keys stored as bf16 (rounded fp32 means) */
 #define QSA_CKEY_FP8 2              /* block keys stored as fp8 E4M3 (rounded, saturated fp32 means) */
+#define QSA_KV_BF16 0               /* K and V rows stored as bf16 */
+#define QSA_KV_FP8 1                /* K and V rows stored as fp8 E4M3 codes, unit scale */
 
 /*
  * Paged KV cache.  Page p of the pool holds, for every KV head, page_size
  * consecutive tokens of one sequence:
- *   k, v   bf16  [num_pages][Hkv][page_size][256]
+ *   k, v   bf16  [num_pages][Hkv][page_size][256]; with kv_dtype QSA_KV_FP8
+ *                fp8 E4M3 codes in the same layout (256 B per row), each code
+ *                being the value itself (unit scale: an fp8 cache without
+ *                calibration scales; the batch-sharded sampling page, section on
+ *                the surrounding patch cluster, records an FP8 main KV cache
+ *                for this attention path).  Every kernel reads them as their
+ *                exact bf16 values: results are those of a bf16 cache holding
+ *                the decoded values.
  *   ckey   fp32  [num_pages][Hkv][page_size / 4][256]   block keys, paged by
  *                the same block table, so a page's keys and block keys never
  *                diverge (the DCP page keeps selector and main cache in one
@@ -100,6 +109,7 @@ typedef struct qsa_kv {
     int32_t max_pages_per_seq;
     int32_t max_seq_len;
     int32_t ckey_dtype;      /* QSA_CKEY_FP32 (0), QSA_CKEY_BF16 (1) or QSA_CKEY_FP8 (2) */
+    int32_t kv_dtype;        /* QSA_KV_BF16 (0) or QSA_KV_FP8 (1) */
 } qsa_kv_t;
 
 /* Library version (major * 10000 + minor * 100 + patch). */

@@ -111,6 +111,28 @@ def bf16_to_f32(a: np.ndarray) -> np.ndarray:
     return (a.astype(np.uint32) << 16).view(np.float32)
 
 
+def bf16_to_e4m3(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp8 E4M3 codes (uint8): round to nearest even, values
+    held within +-448.  How an fp8 cache is filled from bf16 keys and values."""
+    import torch
+
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 26
+    for a in range(0, flat.size, step):
+        t = torch.from_numpy(flat[a:a + step].view(np.int16)).view(torch.bfloat16).float().clamp_(-448.0, 448.0)
+        out[a:a + step] = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return out.reshape(bits.shape)
+
+
+def e4m3_to_bf16(codes: np.ndarray) -> np.ndarray:
+    """fp8 E4M3 codes -> bf16 bit patterns of the same values (exact)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
 def f32_to_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 bit patterns, nearest-even (inputs finite)."""
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -144,6 +166,7 @@ class Case:
     shuffle: bool = True
     shared_prefix_pages: int = 0     # sequence i>0 reuses the first pages of sequence 0
     ckey_dtype: str = "fp32"         # storage of the block keys: "fp32", "bf16" or "fp8"
+    kv_dtype: str = "bf16"           # storage of K and V: "bf16", or "fp8" (E4M3 codes of the bf16 draws)
     block_table: np.ndarray = field(default=None, repr=False)   # int32 [B][max_pages]
     num_pages: int = 0
     _q: Optional[np.ndarray] = field(default=None, repr=False)
@@ -215,13 +238,17 @@ class Case:
             raise RuntimeError("synth_kv failed")
 
     def logical(self, tensor: str, i: int) -> np.ndarray:
-        """bf16 bit patterns [Hkv][L_i][D] of sequence i (tensor 'k' or 'v')."""
+        """bf16 bit patterns [Hkv][L_i][D] of sequence i (tensor 'k' or 'v'): the
+        values the cache holds (with an fp8 cache, the decoded fp8 values)."""
         L = int(self.lens[i])
         if self.shared_prefix_pages and i > 0:
             # content of aliased pages comes from the paged pool: gather it
-            return self.gather_logical(self.paged(tensor), i)
-        out = np.empty((self.Hkv, L, self.D), dtype=np.uint16)
-        self._gen(tensor, i, out, None)
+            out = self.gather_logical(self.paged(tensor), i)
+        else:
+            out = np.empty((self.Hkv, L, self.D), dtype=np.uint16)
+            self._gen(tensor, i, out, None)
+        if self.kv_dtype == "fp8":
+            out = e4m3_to_bf16(bf16_to_e4m3(out))
         return out
 
     def paged(self, tensor: str) -> np.ndarray:
@@ -239,6 +266,12 @@ class Case:
         setattr(self, "_paged_" + tensor, out)
         return out
 
+    def paged_device(self, tensor: str) -> np.ndarray:
+        """The pool as the cache stores it: bf16 bit patterns (uint16), or fp8 E4M3
+        codes (uint8) with kv_dtype "fp8"."""
+        pool = self.paged(tensor)
+        return bf16_to_e4m3(pool) if self.kv_dtype == "fp8" else pool
+
     def drop_paged(self):
         for t in ("k", "v"):
             if hasattr(self, "_paged_" + t):
@@ -255,7 +288,7 @@ class Case:
 def to_device(case: Case, device="cuda", ckey: bool = True):
     """Upload a case's paged pool, tables and queries as torch tensors (layout only).
 
-    Returns a dict: k, v (bf16 [num_pages][Hkv][page_size][D]), ckey (fp32, bf16 or fp8
+    Returns a dict: k, v (bf16, or fp8 E4M3 with kv_dtype "fp8", [num_pages][Hkv][page_size][D]), ckey (fp32, bf16 or fp8
     E4M3 as the case stores block keys, zeroed),
     block_table, seq_lens, q_seq, q_pos (int32), q (bf16 [R][Hq][D])."""
     import torch
@@ -263,9 +296,15 @@ def to_device(case: Case, device="cuda", ckey: bool = True):
     def bf16(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
 
+    def kv(tensor):
+        a = case.paged_device(tensor)
+        if case.kv_dtype == "fp8":
+            return torch.from_numpy(a).view(torch.float8_e4m3fn).to(device)
+        return bf16(a)
+
     out = {
-        "k": bf16(case.paged("k")),
-        "v": bf16(case.paged("v")),
+        "k": kv("k"),
+        "v": kv("v"),
         "block_table": torch.from_numpy(case.block_table).to(device),
         "seq_lens": torch.from_numpy(case.lens).to(device),
         "q_seq": torch.from_numpy(case.q_seq).to(device),
@@ -304,7 +343,7 @@ def _block_table(seed: int, lens: np.ndarray, page_size: int, shuffle: bool, sha
 def make_case(name: str, seed: int, Hq: int, Hkv: int, lens, page_size: int, *, q_seq=None, q_pos=None,
               topk: int = 512, scale: float = 1.0 / 16.0, splits: int = 1, jitter: bool = False,
               bias_frac: float = 0.0, shuffle: bool = True, shared_prefix_pages: int = 0, D: int = 256,
-              ckey_dtype: str = "fp32") -> Case:
+              ckey_dtype: str = "fp32", kv_dtype: str = "bf16") -> Case:
     lens = np.asarray(lens, dtype=np.int32)
     if q_seq is None:  # decode: one row per sequence at its last position
         q_seq = np.arange(lens.shape[0], dtype=np.int32)
@@ -313,7 +352,8 @@ def make_case(name: str, seed: int, Hq: int, Hkv: int, lens, page_size: int, *, 
     return Case(name=name, seed=seed, Hq=Hq, Hkv=Hkv, lens=lens, page_size=page_size,
                 q_seq=np.asarray(q_seq, dtype=np.int32), q_pos=np.asarray(q_pos, dtype=np.int32), topk=topk,
                 scale=scale, splits=splits, D=D, jitter=jitter, bias_frac=bias_frac, shuffle=shuffle,
-                shared_prefix_pages=shared_prefix_pages, block_table=bt, num_pages=num_pages, ckey_dtype=ckey_dtype)
+                shared_prefix_pages=shared_prefix_pages, block_table=bt, num_pages=num_pages, ckey_dtype=ckey_dtype,
+                kv_dtype=kv_dtype)
 
 
 def uniform_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:

@@ -42,6 +42,26 @@ def test_bf16_rounding_is_nearest_even():
         assert synth.lib().synth_bf16_from_float(float(v)) == synth.f32_to_bf16(np.array([v]))[0]
 
 
+def test_fp8_cache_recipe():
+    """An fp8 cache holds the E4M3 codes of the bf16 draws (nearest even, within
+    +-448); the logical view the oracle reads is the decoded values, and decoding
+    is exact.  Codes checked against the format's closed forms."""
+    vals = np.array([1.0, 1.0625, 1.1875, 448.0, 500.0, -1000.0, 2.0 ** -9, 1.5 * 2.0 ** -9, -0.0, 0.0], np.float32)
+    codes = synth.bf16_to_e4m3(synth.f32_to_bf16(vals))
+    assert list(codes) == [0x38, 0x38, 0x3A, 0x7E, 0x7E, 0xFE, 0x01, 0x02, 0x80, 0x00]
+    back = synth.bf16_to_f32(synth.e4m3_to_bf16(codes))
+    assert list(back[:8]) == [1.0, 1.0, 1.25, 448.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -8]
+    allc = np.arange(256, dtype=np.uint8)
+    finite = allc[(allc & 0x7F) != 0x7F]
+    assert np.array_equal(synth.bf16_to_e4m3(synth.e4m3_to_bf16(finite)), finite)  # every code round-trips
+    c = synth.make_case("f8", 3, 16, 2, [100, 37], page_size=16, kv_dtype="fp8", jitter=True)
+    for t in ("k", "v"):
+        pool = c.paged_device(t)
+        assert pool.dtype == np.uint8
+        for i in range(c.B):
+            assert np.array_equal(c.gather_logical(synth.e4m3_to_bf16(pool), i), c.logical(t, i))
+
+
 def test_paged_and_logical_layouts_agree():
     c = synth.config("C2", B=3, L_range=(100, 300))
     pk, pv = c.paged("k"), c.paged("v")
