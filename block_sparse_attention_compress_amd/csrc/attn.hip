@@ -26,7 +26,9 @@
 //                                4q..4q+3 -- 256 contiguous bytes per 16 lanes --
 //                                and output tile n takes dim 128 (n / 8) + 8c +
 //                                n % 8)
-// All K and V loads of a tile are issued before the first wait.  The 4 waves'
+// All K and V loads of a tile are issued before the first wait.  An fp8 cache's
+// rows are read as codes (8 per lane instead of 8 bf16) and widened exactly to
+// bf16 when the tile is staged in LDS; nothing after the staging changes.  The 4 waves'
 // (m, l, O) are merged in LDS and written as the final bf16 output or as an fp32
 // partial (o, lse) for the log-sum-exp merge.
 #include "qsa_device.h"

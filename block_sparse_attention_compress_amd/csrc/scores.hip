@@ -10,9 +10,11 @@
 // Two kernels, both fp32:
 //  * scores_stream_kernel (decode): one row reads its whole block-key list once.
 //    This is the dominant HBM stream of a decode step.  A wave takes 16 blocks
-//    (16 KiB) at a time, each lane one float4 of each block, and folds the 16
-//    dot products with a reduce-scatter butterfly (17 lane exchanges for 16
-//    blocks instead of 16 x 6).
+//    (16 KiB of fp32 keys; 8 KiB bf16, 4 KiB fp8) at a time, each lane 4 dims of
+//    each block, and folds the 16 dot products with a reduce-scatter butterfly
+//    (17 lane exchanges for 16 blocks instead of 16 x 6).  Its REFRESH form also
+//    rebuilds the block key of each sequence's newest token from K (bf16 or fp8
+//    rows) and scores that block with it, replacing a separate compress launch.
 //  * scores_tiled_kernel (extend): many query rows share one sequence, so the
 //    scores are a dense [rows x 256] . [256 x blocks] product; 16x16x4 fp32
 //    matrix-core tiles, 16 rows per wave.
