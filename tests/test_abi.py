@@ -51,6 +51,7 @@ def test_header_constants_match_binding():
     assert int(consts["QSA_CKEY_FP32"]) == qsa.CKEY_FP32 == 0
     assert int(consts["QSA_CKEY_BF16"]) == qsa.CKEY_BF16
     assert int(consts["QSA_CKEY_FP8"]) == qsa.CKEY_FP8 == 2
+    assert int(consts["QSA_KV_BF16"]) == qsa.KV_BF16 == 0 and int(consts["QSA_KV_FP8"]) == qsa.KV_FP8 == 1
 
 
 @pytest.mark.parametrize("over,code", [
@@ -67,6 +68,8 @@ def test_header_constants_match_binding():
     (dict(batch=-1), qsa.QSA_ERR_INVALID_ARG),
     (dict(ckey_dtype=3), qsa.QSA_ERR_INVALID_ARG),
     (dict(ckey_dtype=-1), qsa.QSA_ERR_INVALID_ARG),
+    (dict(kv_dtype=2), qsa.QSA_ERR_INVALID_ARG),
+    (dict(kv_dtype=-1), qsa.QSA_ERR_INVALID_ARG),
 ])
 def test_compress_rejects(over, code):
     d = kv(**over)
