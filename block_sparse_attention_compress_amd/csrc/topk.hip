@@ -10,18 +10,20 @@
 // ascending block order, every block with key > T and the lowest-indexed blocks
 // with key == T.  The result does not depend on thread timing.
 //
-// topk_reg_kernel (rows of up to 65,536 blocks): one 1024-thread workgroup per
-// (row, KV head); the row lives in registers (KPT scores per thread, thread t
-// holding blocks t KPT .. t KPT + KPT - 1, so thread order is block order and
-// one prefix sum of per-thread counts places the output).  Radix digits of raw float keys crowd into a few
+// topk_reg_kernel (rows of up to 65,536 blocks): one workgroup per (row, KV
+// head) -- 1024 threads, or 256 when a launch has many rows -- with the row in
+// registers (KPT scores per thread, thread t holding blocks t KPT .. t KPT +
+// KPT - 1, so thread order is block order and one prefix sum of per-thread
+// counts places the output).  Radix digits of raw float keys crowd into a few
 // exponent bins, and LDS atomics on one address serialise, so the first pass
 // bins uniformly between the row's min and max instead: any monotonic binning
 // keeps the selection exact.  The bin holding the k-th value is then resolved
-// exactly -- by ranking its candidates directly when there are at most 1024 of
-// them, else by exact radix passes restricted to that bin.
+// exactly -- by ranking its candidates directly when there are at most as many
+// as threads, else by exact radix passes restricted to that bin.  The same
+// kernel runs the two stages of the long-row select (below).
 //
-// topk_global_kernel (longer rows): the same select with exact radix passes
-// (11, 11, 10 bits) re-reading the row from L2.
+// topk_global_kernel (longer rows, one stage): the same select with exact radix
+// passes (11, 11, 10 bits) re-reading the row from L2.
 #include <float.h>
 
 #include "block_ops.h"
