@@ -168,3 +168,21 @@ def test_long_prefill_shape_of_the_ascend_tests():
     q_seq, q_pos = synth.extend_rows(total, new)
     case = synth.make_case("prefill7810", 7810, 24, 2, [total], page_size=64, q_seq=q_seq, q_pos=q_pos)
     extend_full(case, [0, 1, 3905, 7808, 7809])
+
+
+def test_longest_sequence_decode():
+    """One sequence at the library's length limit (2^20 tokens, 262,144 blocks per
+    row: two-stage top-k over 32 slices) next to a short one, decode step against
+    the oracle on both rows."""
+    case = synth.make_case("maxlen", 41, 16, 2, [1 << 20, 3001], page_size=64, jitter=True)
+    log(f"max length decode: lens {case.lens.tolist()}")
+    dev, kv = upload(case)
+    qsa.qsa_compress_keys(kv)
+    stride = (max(case.nb(i) for i in range(case.B)) + 63) // 64 * 64
+    buf = DecodeBuffers.allocate(case.B, case.Hq, case.Hkv, stride, case.topk, 0, "cuda")
+    assert buf.topk_workspace is not None
+    decode_step(kv, dev["q"], dev["q_pos"], buf, scale=case.scale)
+    torch.cuda.synchronize()
+    sel, cnt, out, lse = to_np(buf.sel_idx), to_np(buf.sel_cnt), to_np(buf.out), to_np(buf.lse)
+    all_row_properties(case, sel, cnt, out, lse)
+    compare_rows(case, [0, 1], sel, cnt, out, lse, stride)
