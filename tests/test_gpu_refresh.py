@@ -95,3 +95,10 @@ def test_refresh_full_size_decode_workload():
     case = synth.config("C2")
     log(f"C2 refresh: B={case.B}")
     both_paths(case, stride=(max(case.nb(i) for i in range(case.B)) + 63) // 64 * 64, drop_host=True)
+
+
+def test_refresh_with_shared_prefix_pages():
+    """Sequences sharing their first 20 pages (a common prefix): the newest blocks
+    lie in each sequence's own pages, as the refresh launch requires."""
+    case = small_decode("rfpre", 950, 16, 2, [4096, 5000, 4500], 64, shared_prefix_pages=20)
+    both_paths(case)
