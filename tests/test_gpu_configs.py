@@ -186,3 +186,21 @@ def test_longest_sequence_decode():
     sel, cnt, out, lse = to_np(buf.sel_idx), to_np(buf.sel_cnt), to_np(buf.out), to_np(buf.lse)
     all_row_properties(case, sel, cnt, out, lse)
     compare_rows(case, [0, 1], sel, cnt, out, lse, stride)
+
+
+def test_large_batch_decode():
+    """1,024 sequences of 1K-5K tokens, (16,2) heads: 2,048 (row, KV head) units,
+    so the selection takes its many-row form (256 threads per row) and attention
+    one split per unit; against the oracle on sampled rows."""
+    case = synth.make_case("bigbatch", 43, 16, 2, synth.uniform_lengths(43, 1024, 1000, 5000), page_size=64,
+                           jitter=True)
+    log(f"large batch decode: B={case.B}")
+    dev, kv = upload(case)
+    qsa.qsa_compress_keys(kv)
+    stride = (max(case.nb(i) for i in range(case.B)) + 63) // 64 * 64
+    buf = DecodeBuffers.allocate(case.B, case.Hq, case.Hkv, stride, case.topk, 0, "cuda")
+    decode_step(kv, dev["q"], dev["q_pos"], buf, scale=case.scale)
+    torch.cuda.synchronize()
+    sel, cnt, out, lse = to_np(buf.sel_idx), to_np(buf.sel_cnt), to_np(buf.out), to_np(buf.lse)
+    all_row_properties(case, sel, cnt, out, lse)
+    compare_rows(case, [0, 1, 511, 777, 1023], sel, cnt, out, lse, stride)
