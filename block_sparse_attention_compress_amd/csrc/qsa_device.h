@@ -26,6 +26,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Streaming loads: the nontemporal hint keeps data read once (the block-key
+// scan) from being allocated in the caches on its way through.
+typedef float qsa_f4v __attribute__((ext_vector_type(4)));
+typedef unsigned int qsa_u2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+    const qsa_f4v x = __builtin_nontemporal_load(reinterpret_cast<const qsa_f4v*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+    const qsa_u2v x = __builtin_nontemporal_load(reinterpret_cast<const qsa_u2v*>(p));
+    return make_uint2(x[0], x[1]);
+}
+__device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
 // Block-key storage types (qsa_kv_t.ckey_dtype).
 constexpr int kKeyF32 = 0;
 constexpr int kKeyBF16 = 1;

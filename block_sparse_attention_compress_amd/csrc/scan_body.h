@@ -1,6 +1,8 @@
 // One wave's share of the decode block-score scan: 16 blocks at a time, each
 // lane one float4 of each block key, 16 dot products folded by a reduce-scatter
 // butterfly.  Used by scores_stream_kernel and by the fused decode kernel.
+// The keys are read once per step: their loads carry the nontemporal hint
+// (measured at 32 sequences of 32K-64K tokens: 140 -> 122 us).
 #pragma once
 
 #include "qsa_device.h"
@@ -84,14 +86,14 @@ __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int
         if (PAGE16) {
             const Raw* src = keys + gbase[grp] * (kHeadDim / 4) + lane;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = src[j * (kHeadDim / 4)];
+            for (int j = 0; j < 16; ++j) v[j] = load_stream(&src[j * (kHeadDim / 4)]);
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int b = min(b0 + j, n_elig - 1);
                 const int64_t page = bt[b >> lg_bpp];
                 const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
-                v[j] = keys[brow * (kHeadDim / 4) + lane];
+                v[j] = load_stream(&keys[brow * (kHeadDim / 4) + lane]);
             }
         }
     };
