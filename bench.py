@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extend", action="store_true", help="skip the extend (prefill chunk) figures")
-    p.add_argument("--cpu-seconds", type=float, default=4.0, help="target oracle timing span")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle timing span (seconds of wall time)")
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--graph", action="store_true", help="time a replayed HIP graph of the step instead of eager launches")
     p.add_argument("--splits", type=int, default=None, help="decode split count (default: the library's choice)")
