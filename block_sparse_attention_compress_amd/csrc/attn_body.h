@@ -12,7 +12,14 @@ constexpr int kAttnWaves = 4;
 constexpr int kMaxSel = 2048;
 constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
 constexpr int kKRow = kHeadDim + 8;   // padded K row in the LDS tile (elements): spreads rows over banks
-constexpr int kKTile = 16 * kKRow;    // one wave's K (or V) tile (elements)
+constexpr int kKRow8 = kHeadDim + 8;  // padded fp8 row in the LDS tile (bytes)
+// bytes of one staged row: bf16 rows for a bf16 cache, raw codes for an fp8 cache
+template <bool KV8>
+constexpr int kTileRowBytes = KV8 ? kKRow8 : 2 * kKRow;
+// LDS bytes of the 4 waves' K and V staging tiles
+__host__ __device__ constexpr size_t attn_tile_bytes(bool kv8) {
+    return (size_t)kAttnWaves * 2 * 16 * (kv8 ? kTileRowBytes<true> : kTileRowBytes<false>);
+}
 
 typedef short bf16x4s __attribute__((ext_vector_type(4)));
 
@@ -148,8 +155,12 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         sstep = S;
     }
     const int ntiles = (n_s + 15) / 16;
-    uint16_t* ktile = reinterpret_cast<uint16_t*>(smem + P.table_words) + wave * 2 * kKTile;
-    uint16_t* vtile = ktile + kKTile;
+    typedef typename KVRaw<KV8>::type Raw;  // 8 elements of a row, as loaded and as staged
+    // this wave's K and V staging tiles: 16 rows of RB bytes each
+    constexpr int RB = kTileRowBytes<KV8>;
+    constexpr int EB = KV8 ? 1 : 2;  // bytes per element
+    uint8_t* ktile = reinterpret_cast<uint8_t*>(smem + P.table_words) + wave * 2 * 16 * RB;
+    uint8_t* vtile = ktile + 16 * RB;
 
     float m_run = -INFINITY;  // reference max of head c (log2 units), same in every qq group
     float l_run = 0.f;        // this lane's share of the head's normaliser
@@ -157,90 +168,35 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Raw tile loads are coalesced -- instruction j covers the 1 KiB of tile rows
-    // 2j and 2j+1 -- and land in this wave's LDS tiles, from which the MFMA
-    // layouts are read.  The loads of tile i+1 are issued before tile i is
-    // computed, so a wave always has a tile in flight.
-    // (the raw tile is 16 named registers, not an array: an array indexed in a
-    // loop across the tile pipeline was kept in scratch memory)
-    // (fp8 rows are 256 bytes: each lane reads 8 codes and widens them to bf16 as
-    // they are staged, so the tiles and everything after them are the same)
-    typedef typename KVRaw<KV8>::type Raw;
-    Raw k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
-#define QSA_LOAD_J(J, KX, VX)                                                               \
-    do {                                                                                    \
-        const int nr = n0_ + 2 * (J) + (lane >> 5);                                         \
-        const int rr = nr < n_s ? slot_row[slot0 + sstep * nr] : -1;                        \
-        const int64_t off = (int64_t)max(rr, 0) * kHeadDim + 8 * (lane & 31);               \
-        if (KV8) {                                                                          \
-            KX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.k) + off); \
-            VX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.v) + off); \
-        } else {                                                                            \
-            KX = *reinterpret_cast<const Raw*>(P.k + off);                                  \
-            VX = *reinterpret_cast<const Raw*>(P.v + off);                                  \
-        }                                                                                   \
-    } while (0)
-#define QSA_LOAD_RAW(TILE, RV)                                                              \
-    do {                                                                                    \
-        const int n0_ = (TILE) * 16;                                                        \
-        QSA_LOAD_J(0, k0, v0);                                                       \
-        QSA_LOAD_J(1, k1, v1);                                                       \
-        QSA_LOAD_J(2, k2, v2);                                                       \
-        QSA_LOAD_J(3, k3, v3);                                                       \
-        QSA_LOAD_J(4, k4, v4);                                                       \
-        QSA_LOAD_J(5, k5, v5);                                                       \
-        QSA_LOAD_J(6, k6, v6);                                                       \
-        QSA_LOAD_J(7, k7, v7);                                                       \
-        /* masks of the tokens whose scores / weights this lane owns: 4 qq + i */          \
-        RV[0] = n0_ + 4 * qq + 0 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 0)] : -1;  \
-        RV[1] = n0_ + 4 * qq + 1 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 1)] : -1;  \
-        RV[2] = n0_ + 4 * qq + 2 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 2)] : -1;  \
-        RV[3] = n0_ + 4 * qq + 3 < n_s ? slot_row[slot0 + sstep * (n0_ + 4 * qq + 3)] : -1;  \
-    } while (0)
-#define QSA_STAGE_J(J, KX, VX)                                                              \
-    do {                                                                                    \
-        const int r = 2 * (J) + (lane >> 5);                                                \
-        *reinterpret_cast<uint4*>(ktile + r * kKRow + 8 * (lane & 31)) = kv_bf16x8(KX);     \
-        *reinterpret_cast<uint4*>(vtile + r * kKRow + 8 * (lane & 31)) = kv_bf16x8(VX);     \
-    } while (0)
-    int rv_cur[4], rv_nxt[4];
-    QSA_LOAD_RAW(wave, rv_cur);
-    for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
-        // ---- stage the arrived tile (a masked row holds row 0's bytes: its weight
-        // is zeroed below and its V slice too)
-        QSA_STAGE_J(0, k0, v0);
-        QSA_STAGE_J(1, k1, v1);
-        QSA_STAGE_J(2, k2, v2);
-        QSA_STAGE_J(3, k3, v3);
-        QSA_STAGE_J(4, k4, v4);
-        QSA_STAGE_J(5, k5, v5);
-        QSA_STAGE_J(6, k6, v6);
-        QSA_STAGE_J(7, k7, v7);
-        // past the last tile every slot reads as masked: the loads then all hit
-        // row 0 (one cached line) and no branch breaks the register pipeline
-        QSA_LOAD_RAW(tile + kAttnWaves, rv_nxt);
-        int rv[4];
+    // One 16-token tile, staged in this wave's LDS tiles: S^T = K Q^T, the online
+    // softmax, O += P V.  Bit i of `live` clear masks token 4 qq + i (its staged
+    // bytes may be anything: its weight and its V slice are zeroed).
+    auto compute_tile = [&](int live) {
+        auto k_operand = [&](int m) {
+            const uint4 x = kv_bf16x8(*reinterpret_cast<const Raw*>(ktile + c * RB + EB * (32 * m + 8 * qq)));
+            return __builtin_bit_cast(bf16x8, x);
+        };
+        // ---- S^T = K . Q^T: st[i] = S[head c][token n0 + 4 qq + i]
+        floatx4 st = {0.f, 0.f, 0.f, 0.f};
+        {
+            bf16x8 kb[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rv[i] = rv_cur[i];
-        bf16x8 kb[8];
+            for (int m = 0; m < 8; ++m) kb[m] = k_operand(m);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) kb[m] = *reinterpret_cast<const bf16x8*>(ktile + c * kKRow + 32 * m + 8 * qq);
+            for (int m = 0; m < 8; ++m) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[m], qb[m], st, 0, 0, 0);
+        }
         uint4 vv[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint16_t* vr = vtile + (4 * qq + i) * kKRow + 8 * c;
-            vv[i][0] = *reinterpret_cast<const uint4*>(vr);
-            vv[i][1] = *reinterpret_cast<const uint4*>(vr + 128);
+            const uint8_t* vr = vtile + (4 * qq + i) * RB + EB * 8 * c;
+            vv[i][0] = kv_bf16x8(*reinterpret_cast<const Raw*>(vr));
+            vv[i][1] = kv_bf16x8(*reinterpret_cast<const Raw*>(vr + EB * 128));
         }
-        // ---- S^T = K . Q^T: st[i] = S[head c][token n0 + 4 qq + i]
-        floatx4 st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 8; ++m) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[m], qb[m], st, 0, 0, 0);
         float x[4];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = rv[i] >= 0 ? st[i] * P.scale_log2 : -INFINITY;
+            x[i] = (live >> i) & 1 ? st[i] * P.scale_log2 : -INFINITY;
             mx = fmaxf(mx, x[i]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -272,7 +228,7 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         // ---- zero the V of masked slots (their weight is 0, their bytes may be anything)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (rv[i] < 0) {
+            if (!((live >> i) & 1)) {
                 vv[i][0] = make_uint4(0, 0, 0, 0);
                 vv[i][1] = make_uint4(0, 0, 0, 0);
             }
@@ -299,8 +255,66 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
             }
             O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nt], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rv_cur[i] = rv_nxt[i];
+    };
+
+    // Raw tile loads are coalesced -- instruction j covers tile rows 2j and 2j+1
+    // (1 KiB of bf16, 512 B of fp8) -- and land in this wave's LDS tiles, from
+    // which the MFMA layouts are read.  The loads of tile i+1 are issued before
+    // tile i is computed, so a wave always has a tile in flight.  fp8 rows are
+    // staged as codes and widened to bf16 as the MFMA operands are read, which
+    // halves their LDS traffic.
+    // (the raw tile is 16 named registers, not an array: an array indexed in a
+    // loop across the tile pipeline was kept in scratch memory)
+    Raw k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+#define QSA_LOAD_J(J, KX, VX)                                                               \
+    do {                                                                                    \
+        const int nr = n0_ + 2 * (J) + (lane >> 5);                                         \
+        const int rr = nr < n_s ? slot_row[slot0 + sstep * nr] : -1;                        \
+        const int64_t off = (int64_t)max(rr, 0) * kHeadDim * EB + sizeof(Raw) * (lane & 31); \
+        KX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.k) + off);    \
+        VX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.v) + off);    \
+    } while (0)
+#define QSA_LOAD_RAW(TILE, LIVE)                                                            \
+    do {                                                                                    \
+        const int n0_ = (TILE) * 16;                                                        \
+        QSA_LOAD_J(0, k0, v0);                                                              \
+        QSA_LOAD_J(1, k1, v1);                                                              \
+        QSA_LOAD_J(2, k2, v2);                                                              \
+        QSA_LOAD_J(3, k3, v3);                                                              \
+        QSA_LOAD_J(4, k4, v4);                                                              \
+        QSA_LOAD_J(5, k5, v5);                                                              \
+        QSA_LOAD_J(6, k6, v6);                                                              \
+        QSA_LOAD_J(7, k7, v7);                                                              \
+        /* which of the tokens 4 qq + i, whose scores / weights this lane owns, are live */ \
+        LIVE = 0;                                                                           \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                  \
+            const int n_ = n0_ + 4 * qq + i_;                                               \
+            LIVE |= (n_ < n_s && slot_row[slot0 + sstep * n_] >= 0) << i_;                  \
+        }                                                                                   \
+    } while (0)
+#define QSA_STAGE_J(J, KX, VX)                                                              \
+    do {                                                                                    \
+        const int r = 2 * (J) + (lane >> 5);                                                \
+        *reinterpret_cast<Raw*>(ktile + r * RB + sizeof(Raw) * (lane & 31)) = KX;           \
+        *reinterpret_cast<Raw*>(vtile + r * RB + sizeof(Raw) * (lane & 31)) = VX;           \
+    } while (0)
+    // past the last tile every slot reads as masked: the loads then all hit row 0
+    // (one cached line) and no branch breaks the register pipeline; a masked row
+    // holds row 0's bytes, whose weight and V slice are zeroed
+    int live_next;
+    QSA_LOAD_RAW(wave, live_next);
+    for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
+        QSA_STAGE_J(0, k0, v0);
+        QSA_STAGE_J(1, k1, v1);
+        QSA_STAGE_J(2, k2, v2);
+        QSA_STAGE_J(3, k3, v3);
+        QSA_STAGE_J(4, k4, v4);
+        QSA_STAGE_J(5, k5, v5);
+        QSA_STAGE_J(6, k6, v6);
+        QSA_STAGE_J(7, k7, v7);
+        const int live = live_next;
+        QSA_LOAD_RAW(tile + kAttnWaves, live_next);
+        compute_tile(live);
     }
 #undef QSA_LOAD_RAW
 #undef QSA_LOAD_J
