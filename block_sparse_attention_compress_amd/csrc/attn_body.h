@@ -62,13 +62,19 @@ struct KVRaw<true> {
     typedef uint2 type;
 };
 
-// 8 elements as bf16: fp8 codes are widened exactly (an E4M3 value has at most 4
-// significant bits, so the top half of its fp32 form is its bf16 form).
+// 8 elements as bf16.  fp8 codes are widened exactly (every E4M3 value is a bf16
+// value), two per instruction: the scaled fp8 -> bf16 conversion with a scale of
+// 1 takes the two codes of one 16-bit half of a word (low half: first code in
+// the low bf16).
 __device__ __forceinline__ uint4 kv_bf16x8(const uint4& x) { return x; }
 __device__ __forceinline__ uint4 kv_bf16x8(const uint2& x) {
-    const float4 a = unpack_fp8x4(x.x), b = unpack_fp8x4(x.y);
-    auto pair = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u); };
-    return make_uint4(pair(a.x, a.y), pair(a.z, a.w), pair(b.x, b.y), pair(b.z, b.w));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
+    return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                      __builtin_bit_cast(uint32_t, d));
 }
 
 // LDS: `smem` is dynamic shared memory of the launch: the slot table (16 B per
@@ -246,13 +252,11 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
             const uint32_t d2 = u4_word(vv[2][hf], e), d3 = u4_word(vv[3][hf], e);
             bf16x4s vb;
             uint32_t* v32 = reinterpret_cast<uint32_t*>(&vb);
-            if (nt & 1) {
-                v32[0] = (d0 >> 16) | (d1 & 0xffff0000u);
-                v32[1] = (d2 >> 16) | (d3 & 0xffff0000u);
-            } else {
-                v32[0] = (d0 & 0xffffu) | (d1 << 16);
-                v32[1] = (d2 & 0xffffu) | (d3 << 16);
-            }
+            // one byte permute per word: the low (even nt) or high (odd nt) bf16 of
+            // each of two tokens' dwords
+            constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
+            v32[0] = __builtin_amdgcn_perm(d1, d0, (nt & 1) ? kHi : kLo);
+            v32[1] = __builtin_amdgcn_perm(d3, d2, (nt & 1) ? kHi : kLo);
             O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nt], 0, 0, 0);
         }
     };
