@@ -270,17 +270,29 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
     // (the raw tile is 16 named registers, not an array: an array indexed in a
     // loop across the tile pipeline was kept in scratch memory)
     Raw k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+    // The slot reads are unconditional (index clamped to the last slot, result
+    // masked after), so that the 12 LDS reads of a tile issue back to back rather
+    // than one round trip per load, and the next tile's are issued before this
+    // tile's staging writes.  Slot 0 exists in the table, or in the tiles after
+    // it, even when n_s is 0.
+    const int last_slot = max(n_s - 1, 0);
+    int n0_, rr_[8], lv_[4];
+#define QSA_SLOT(N) slot_row[slot0 + sstep * min((N), last_slot)]
+#define QSA_SLOTS(TILE)                                                                     \
+    do {                                                                                    \
+        n0_ = (TILE) * 16;                                                                  \
+        _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rr_[j_] = QSA_SLOT(n0_ + 2 * j_ + (lane >> 5)); \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) lv_[i_] = QSA_SLOT(n0_ + 4 * qq + i_); \
+    } while (0)
 #define QSA_LOAD_J(J, KX, VX)                                                               \
     do {                                                                                    \
-        const int nr = n0_ + 2 * (J) + (lane >> 5);                                         \
-        const int rr = nr < n_s ? slot_row[slot0 + sstep * nr] : -1;                        \
+        const int rr = n0_ + 2 * (J) + (lane >> 5) < n_s ? rr_[J] : -1;                     \
         const int64_t off = (int64_t)max(rr, 0) * kHeadDim * EB + sizeof(Raw) * (lane & 31); \
         KX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.k) + off);    \
         VX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.v) + off);    \
     } while (0)
-#define QSA_LOAD_RAW(TILE, LIVE)                                                            \
+#define QSA_LOAD_RAW(LIVE)                                                                  \
     do {                                                                                    \
-        const int n0_ = (TILE) * 16;                                                        \
         QSA_LOAD_J(0, k0, v0);                                                              \
         QSA_LOAD_J(1, k1, v1);                                                              \
         QSA_LOAD_J(2, k2, v2);                                                              \
@@ -291,10 +303,8 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         QSA_LOAD_J(7, k7, v7);                                                              \
         /* which of the tokens 4 qq + i, whose scores / weights this lane owns, are live */ \
         LIVE = 0;                                                                           \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                  \
-            const int n_ = n0_ + 4 * qq + i_;                                               \
-            LIVE |= (n_ < n_s && slot_row[slot0 + sstep * n_] >= 0) << i_;                  \
-        }                                                                                   \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                    \
+            LIVE |= (n0_ + 4 * qq + i_ < n_s && lv_[i_] >= 0) << i_;                         \
     } while (0)
 #define QSA_STAGE_J(J, KX, VX)                                                              \
     do {                                                                                    \
@@ -306,8 +316,10 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
     // (one cached line) and no branch breaks the register pipeline; a masked row
     // holds row 0's bytes, whose weight and V slice are zeroed
     int live_next;
-    QSA_LOAD_RAW(wave, live_next);
+    QSA_SLOTS(wave);
+    QSA_LOAD_RAW(live_next);
     for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
+        QSA_SLOTS(tile + kAttnWaves);
         QSA_STAGE_J(0, k0, v0);
         QSA_STAGE_J(1, k1, v1);
         QSA_STAGE_J(2, k2, v2);
@@ -317,11 +329,13 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         QSA_STAGE_J(6, k6, v6);
         QSA_STAGE_J(7, k7, v7);
         const int live = live_next;
-        QSA_LOAD_RAW(tile + kAttnWaves, live_next);
+        QSA_LOAD_RAW(live_next);
         compute_tile(live);
     }
 #undef QSA_LOAD_RAW
 #undef QSA_LOAD_J
+#undef QSA_SLOT
+#undef QSA_SLOTS
 #undef QSA_STAGE_J
 
     // ---- merge the 4 waves in LDS.  Per head: M = the largest reference max of
