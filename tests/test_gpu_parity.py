@@ -312,6 +312,43 @@ def test_split_partials_merge_and_unsplit(S):
         np.testing.assert_allclose(ref.out[r], ref1.out[r], atol=1e-12)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_splits_without_tokens(kv_dtype):
+    """16 splits over sequences of 1 to 33 tokens (1 to 9 blocks selected): most
+    splits hold no token, and their partials must be 0 with lse -inf, as the oracle
+    gives.  The merged partials and the library's internal 16-way split must still
+    equal the oracle."""
+    import block_sparse_attention_compress_amd as qsa
+    S = 16
+    case = small_decode(f"s16{kv_dtype}", 77, 16, 2, [1, 5, 9, 33], 64, jitter=True, kv_dtype=kv_dtype)
+    log(f"16 splits, few tokens, {kv_dtype} cache")
+    d = Dev(case)
+    d.compress()
+    sc = d.scores()
+    sel, cnt = d.topk(sc, 512)
+    po, pl = d.decode_partials(sel, cnt, 512, S)
+    N = case.B * case.Hq
+    merged = torch.empty((case.B, case.Hq, 256), dtype=torch.bfloat16, device="cuda")
+    mlse = torch.empty((case.B, case.Hq), dtype=torch.float32, device="cuda")
+    qsa.qsa_merge_lse(po, pl, S, N, 256, merged, mlse)
+    internal, ilse = d.decode_attn(sel, cnt, 512, num_splits=S)
+    torch.cuda.synchronize()
+    sel_np, cnt_np = to_np(sel), to_np(cnt)
+    assert np.array_equal(cnt_np[:, 0], [1, 2, 3, 9]) and np.array_equal(cnt_np[:, 1], [1, 2, 3, 9])
+    override = {(r, h): (sel_np[r, h], int(cnt_np[r, h])) for r in range(case.R) for h in range(case.Hkv)}
+    ref = oracle.run_case(case, splits=S, sel_override=override)
+    po, pl = to_np(po), to_np(pl)
+    for r in range(case.R):
+        n_tok = int(case.lens[r])
+        for s_ in range(n_tok, S):  # token p goes to split p mod S: these splits are empty
+            assert np.all(po[s_, r] == 0) and np.all(np.isneginf(pl[s_, r])), (r, s_)
+        check_close(po[:, r], ref.part_out[r], f"partials row {r}")
+        check_lse(pl[:, r], ref.part_lse[r], f"partial lse row {r}")
+        for name, o, l in (("merged", merged, mlse), ("internal", internal, ilse)):
+            check_close(to_np(o)[r], ref.out[r], f"{name} row {r}")
+            check_lse(to_np(l)[r], ref.lse[r], f"{name} lse row {r}")
+
+
 def test_merge_kernel_against_oracle_with_empty_partials():
     import block_sparse_attention_compress_amd as qsa
     rng = np.random.default_rng(3)
