@@ -65,30 +65,34 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
                                             scores + ((int64_t)row * Hkv + h) * score_stride, rf);
 }
 
-// Extend: 64 rows per workgroup, 16 per wave, and kTiledChunk blocks per
-// workgroup (grid z), so a chunk of new tokens spreads over every CU.  Lane
+// Extend: 16 rows per wave, kTiledWaves waves (64 rows) per workgroup, and
+// kTiledChunk blocks per workgroup (grid z), so a chunk of new tokens spreads
+// over every CU.  Lane
 // (c = lane & 15, kq = lane >> 4) holds, at k-step m, qsum[row c][64 kq + m] (A
 // operand) and ckey[block c][64 kq + m] (B operand): the same dim for A and B, so
 // the 64 steps of the 16x16x4 matrix-core op cover all 256 dims.  Output element
 // i of the lane is row 4 kq + i, block c of the tile.
 //
-// When the workgroup's 64 rows belong to one sequence (the usual extend chunk),
-// its 4 waves share each 16-block tile of keys: the 256 threads load it together
-// (4 float4 each), it is staged in LDS (fp32, rows padded against bank
-// conflicts), and two tiles are in flight while one is multiplied.  Otherwise
-// each wave streams its own tiles, and rows of one wave that belong to different
-// sequences are scored in separate passes.
+// When the workgroup's rows belong to one sequence (the usual extend chunk), its
+// waves share each 16-block tile of keys: the threads load it together, it is
+// staged in LDS (fp32, rows padded against bank conflicts), and two tiles are in
+// flight while one is multiplied.  Otherwise each wave streams its own tiles, a
+// quarter (16 dims) at a time so that this path needs few registers, and rows of
+// one wave that belong to different sequences are scored in separate passes.
 constexpr int kTiledChunk = 512;
+constexpr int kTiledWaves = 4;  // waves (16 query rows each) per workgroup (8: slower)
 constexpr int kTRow = kHeadDim + 4;  // padded key row of an LDS tile (floats)
 
-template <int KT>
-__global__ __launch_bounds__(256) void scores_tiled_kernel(
+template <int KT, int NW>
+__global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int R, int g, const void* __restrict__ ckey,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages,
     float* __restrict__ scores, int score_stride) {
     __shared__ float ktile[2][16 * kTRow];
-    __shared__ int w_smin[4], w_smax[4], w_nend[4];
+    __shared__ int w_smin[NW], w_smax[NW], w_nend[NW];
+    constexpr int TPB = 4 * NW;        // threads per block key of a staged tile
+    constexpr int FPT = 64 / TPB;      // float4 (Raw) pieces per thread
     typedef typename KeyRaw<KT>::type Raw;
     const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
     const int h = blockIdx.y;
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = wave_id();
-    const int r0 = blockIdx.x * 64 + wave * 16;
+    const int r0 = blockIdx.x * (16 * NW) + wave * 16;
     const int c = lane & 15, kq = lane >> 4;
     const int row = r0 + c;
     const bool valid = row < R;
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
     __syncthreads();
     int smin = w_smin[0], smax = w_smax[0], wg_end = w_nend[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < NW; ++w) {
         smin = min(smin, w_smin[w]);
         smax = max(smax, w_smax[w]);
         wg_end = max(wg_end, w_nend[w]);
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
         const int wave_end = min(wave_max_int(ne_c), bc0 + kTiledChunk);
         const int ntiles = (wg_end - bc0 + 15) / 16;
         // this thread's share of a tile: block bl, float4 slots f0 + 16 j of its key
-        const int bl = tid >> 4, f0 = tid & 15;
+        const int bl = tid / TPB, f0 = tid % TPB;
         auto load = [&](int t, Raw* gr) {
             const int b = bc0 + 16 * t + bl;
             if (b < nb_seq) {
@@ -177,16 +181,16 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
                 const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
                 const Raw* src = keys + brow * (kHeadDim / 4) + f0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) gr[j] = src[16 * j];
+                for (int j = 0; j < FPT; ++j) gr[j] = src[TPB * j];
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) gr[j] = Raw{};
+                for (int j = 0; j < FPT; ++j) gr[j] = Raw{};
             }
         };
         auto stage = [&](int slot, const Raw* gr) {
             float* dst = ktile[slot] + bl * kTRow + 4 * f0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) *reinterpret_cast<float4*>(dst + 64 * j) = key4(gr[j]);
+            for (int j = 0; j < FPT; ++j) *reinterpret_cast<float4*>(dst + 4 * TPB * j) = key4(gr[j]);
         };
         auto compute = [&](int t, int slot) {
             const int bt0 = bc0 + 16 * t;
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
         // two register sets (named, so nothing is indexed across iterations) and two
         // LDS slots: tile t is multiplied from slot t % 2 while tiles t + 1 and t + 2
         // are in flight
-        Raw g0[4], g1[4];
+        Raw g0[FPT], g1[FPT];
         load(0, g0);
         if (ntiles > 1) load(1, g1);
         stage(0, g0);
@@ -242,41 +246,52 @@ __global__ __launch_bounds__(256) void scores_tiled_kernel(
         int ne_out[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ne_out[i] = __shfl(ne_c, 4 * kq + i);
-        // block keys of the tile at bt0 into v, raw (zeros past the sequence)
-        auto load_tile = [&](int bt0, Raw* v) {
+        // a quarter of the keys of the tile at bt0 (dims 64 kq + 16 qt .. + 15 of
+        // block bt0 + c) into v, raw (zeros past the sequence).  One quarter is in
+        // flight while the previous one is multiplied, which keeps this path's
+        // registers (and so the kernel's) low.
+        auto load_q = [&](int bt0, int qt, Raw* v) {
             const int b = bt0 + c;
             if (b < nb_seq) {
                 const int64_t page = block_table[(int64_t)s * max_pages + (b >> lg_bpp)];
                 const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
-                const Raw* src = keys + brow * (kHeadDim / 4) + 16 * kq;
+                const Raw* src = keys + brow * (kHeadDim / 4) + 16 * kq + 4 * qt;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = src[i];
+                for (int i = 0; i < 4; ++i) v[i] = src[i];
             } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = Raw{};
+                for (int i = 0; i < 4; ++i) v[i] = Raw{};
             }
         };
-        Raw cur[16], nxt[16];
-        if (bc0 < n_end) load_tile(bc0, cur);
-        for (int bt0 = bc0; bt0 < n_end; bt0 += 16) {
-            if (bt0 + 16 < n_end) load_tile(bt0 + 16, nxt);
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        // k-steps 16 qt .. 16 qt + 15 of the 16x16x4 product
+        auto mma_q = [&](int qt, const Raw* v, floatx4& acc) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float4 kv = key4(cur[i]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 0], kv.x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 1], kv.y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 2], kv.z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 3], kv.w, acc, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const float4 kv = key4(v[i]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[16 * qt + 4 * i + 0], kv.x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[16 * qt + 4 * i + 1], kv.y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[16 * qt + 4 * i + 2], kv.z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[16 * qt + 4 * i + 3], kv.w, acc, 0, 0, 0);
             }
+        };
+        Raw qa[4], qb[4];
+        if (bc0 < n_end) load_q(bc0, 0, qa);
+        for (int bt0 = bc0; bt0 < n_end; bt0 += 16) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            load_q(bt0, 1, qb);
+            mma_q(0, qa, acc);
+            load_q(bt0, 2, qa);
+            mma_q(1, qb, acc);
+            load_q(bt0, 3, qb);
+            mma_q(2, qa, acc);
+            if (bt0 + 16 < n_end) load_q(bt0 + 16, 0, qa);
+            mma_q(3, qb, acc);
             const int b = bt0 + c;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = 4 * kq + i;
                 if (b < ne_out[i]) scores[((int64_t)(r0 + rr) * Hkv + h) * score_stride + b] = acc[i];
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
         }
     }
 }
@@ -319,9 +334,10 @@ hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scor
 hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* scores, int score_stride,
                                hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
-    dim3 grid((rows.R + 63) / 64, kv.Hkv, (score_stride + kTiledChunk - 1) / kTiledChunk);
+    dim3 grid((rows.R + 16 * kTiledWaves - 1) / (16 * kTiledWaves), kv.Hkv, (score_stride + kTiledChunk - 1) / kTiledChunk);
 #define QSA_TILED(KT)                                                                                            \
-    hipLaunchKernelGGL(scores_tiled_kernel<KT>, grid, dim3(256), 0, st, rows.q, rows.q_stride, rows.q_seq,       \
+    hipLaunchKernelGGL((scores_tiled_kernel<KT, kTiledWaves>), grid, dim3(64 * kTiledWaves), 0, st, rows.q,       \
+                       rows.q_stride, rows.q_seq,                                                                \
                        rows.q_pos, rows.R, rows.Hq / kv.Hkv, kv.ckey, kv.block_table, kv.seq_lens, kv.Hkv, kv.lg_ps, \
                        kv.max_pages, scores, score_stride)
     if (kv.ckey_type == kKeyFP8)
