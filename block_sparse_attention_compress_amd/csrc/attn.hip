@@ -15,7 +15,7 @@
 // masked slot).  A wave then takes 16 selected tokens at a time:
 //   S^T[token][head] = K . Q^T   8 x v_mfma_f32_16x16x32_bf16; MFMA m covers dims
 //                                32m..32m+31, lane (r, q) giving dims 32m + 8q..+7
-//                                of token r, so each load instruction reads 64
+//                                of token r, so each operand read covers 64
 //                                contiguous bytes of each of the 16 K rows
 //   online softmax in fp32, base 2 (x * scale * log2 e), with a lazy reference
 //                                max: O and l are rescaled only when a head's
@@ -26,11 +26,13 @@
 //                                4q..4q+3 -- 256 contiguous bytes per 16 lanes --
 //                                and output tile n takes dim 128 (n / 8) + 8c +
 //                                n % 8)
-// All K and V loads of a tile are issued before the first wait.  An fp8 cache's
-// rows are read as codes (8 per lane instead of 8 bf16) and widened exactly to
-// bf16 when the tile is staged in LDS; nothing after the staging changes.  The 4 waves'
-// (m, l, O) are merged in LDS and written as the final bf16 output or as an fp32
-// partial (o, lse) for the log-sum-exp merge.
+// The raw K and V rows of a tile are loaded coalesced, all before the first wait
+// (their row indices come from the slot table in back-to-back LDS reads), and
+// staged in a per-wave LDS tile from which the operands above are read.  An fp8
+// cache's rows are loaded and staged as codes (8 per lane instead of 8 bf16) and
+// widened exactly to bf16, two codes per conversion, as the operands are read.
+// The 4 waves' (m, l, O) are merged in LDS and written as the final bf16 output or
+// as an fp32 partial (o, lse) for the log-sum-exp merge.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 #include "attn_body.h"
