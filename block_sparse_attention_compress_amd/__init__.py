@@ -99,9 +99,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_decode_fused_workspace_bytes.argtypes = [kvp, i32, i32, i32]
         L.qsa_decode_fused_workspace_bytes.restype = sz
         for f in ("qsa_compress_keys", "qsa_block_scores", "qsa_decode_scores_refresh", "qsa_topk_blocks",
-                  "qsa_topk_blocks_ws",
-                  "qsa_sparse_attn_decode",
-                  "qsa_sparse_attn_extend", "qsa_merge_lse", "qsa_decode_fused"):
+                  "qsa_topk_blocks_ws", "qsa_sparse_attn_decode", "qsa_sparse_attn_extend", "qsa_merge_lse",
+                  "qsa_decode_fused"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
