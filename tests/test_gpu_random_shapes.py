@@ -4,7 +4,9 @@ Each case draws its head pair (group sizes 1 to 16, including the pages' pairs),
 page size, batch, lengths (1 to 6,000 tokens, sometimes 0), k, split count,
 block-key storage and cache storage at once, so combinations that the targeted
 tests do not enumerate are covered too.  Decode cases run the step of the
-separate calls; extend cases put several sequences' new rows in one launch.
+separate calls, and some of them the fused single launch as well (its selection
+equal to the separate calls' bit for bit); extend cases put several sequences'
+new rows in one launch.
 The bars are those of the targeted parity tests: the selection bit-exact on the
 GPU's own fp32 scores and within the 1e-4 swap window against the oracle,
 outputs and lse within |gpu - oracle| <= 1e-2 + 1e-2 |oracle|."""
@@ -80,3 +82,12 @@ def test_random_extend_shapes(i):
         f"rows={case.R} k={k} keys={case.ckey_dtype} cache={case.kv_dtype}")
     res = run_extend(case, k=k)
     check_decode_against_oracle(case, *res, k)
+
+
+@pytest.mark.parametrize("i", range(0, 24, 3))
+def test_random_decode_shapes_fused(i):
+    from test_gpu_fused import check_fused
+    case, k, splits = random_decode(i)
+    log(f"random fused {i}: heads=({case.Hq},{case.Hkv}) page={case.page_size} lens={case.lens.tolist()} k={k} "
+        f"splits={splits} keys={case.ckey_dtype} cache={case.kv_dtype}")
+    check_fused(case, k=k, num_splits=splits)
