@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extend", action="store_true", help="skip the extend (prefill chunk) figures")
+    p.add_argument("--extend-only", action="store_true",
+                   help="print only the extend chunk's figures (one JSON object; for profiling the chunk alone)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle timing span (seconds of wall time)")
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--graph", action="store_true", help="time a replayed HIP graph of the step instead of eager launches")
@@ -248,6 +250,10 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.extend_only:
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        print(json.dumps(extend_figures(args.steps, args.flush, args.ckey, args.kv)), flush=True)
         return
     import block_sparse_attention_compress_amd as qsa
     import synth
