@@ -11,7 +11,7 @@
 // with key == T.  The result does not depend on thread timing.
 //
 // topk_reg_kernel (rows of up to 65,536 blocks): one workgroup per (row, KV
-// head) -- 1024 threads, or 256 when a launch has many rows -- with the row in
+// head) -- 1024 threads, or 512 when a launch has many rows -- with the row in
 // registers (KPT scores per thread, thread t holding blocks t KPT .. t KPT +
 // KPT - 1, so thread order is block order and one prefix sum of per-thread
 // counts places the output).  Radix digits of raw float keys crowd into a few
@@ -77,7 +77,7 @@ __device__ __forceinline__ int eligible(const int32_t* q_pos, int row, int score
 // ------------------------------------------------------------------ registers
 
 constexpr int kRegThreads = 1024;  // threads per row, unless many rows share the launch
-constexpr int kManyThreads = 256;  // threads per row when rows are many (extend chunks)
+constexpr int kManyThreads = 512;  // threads per row when rows are many (extend chunks)
 constexpr int kBins = 2048;
 
 // Candidate workspace of the two-stage select for long rows: per (row, KV head),
@@ -445,8 +445,9 @@ static void launch_reg(int per, dim3 grid, const float* scores, int score_stride
 #undef QSA_TOPK_REG
 }
 
-// With many rows per launch (an extend chunk), 256-thread workgroups let 8 rows
-// share a CU and hide each other's latency; with few, 1024 threads shorten each row.
+// With many rows per launch (an extend chunk), 512-thread workgroups let several
+// rows share a CU and hide each other's latency (256 and 128 threads were slower);
+// with few rows, 1024 threads shorten each row.
 constexpr int kManyRows = 1024;
 
 hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,

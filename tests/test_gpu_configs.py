@@ -190,7 +190,7 @@ def test_longest_sequence_decode():
 
 def test_large_batch_decode():
     """1,024 sequences of 1K-5K tokens, (16,2) heads: 2,048 (row, KV head) units,
-    so the selection takes its many-row form (256 threads per row) and attention
+    so the selection takes its many-row form (512 threads per row) and attention
     one split per unit; against the oracle on sampled rows."""
     case = synth.make_case("bigbatch", 43, 16, 2, synth.uniform_lengths(43, 1024, 1000, 5000), page_size=64,
                            jitter=True)

@@ -127,9 +127,9 @@ def test_workspace_reused_by_a_smaller_call():
         check(sc, None, 512, ws=ws)
 
 
-def test_many_rows_use_the_256_thread_kernel_bit_exact():
-    """1,100 rows of one KV head: the launch takes 256 threads per row.  Random,
-    heavily tied (bins crowded past 256 candidates: the radix passes), all-equal
+def test_many_rows_use_the_many_row_kernel_bit_exact():
+    """1,100 rows of one KV head: the launch takes 512 threads per row.  Random,
+    heavily tied (bins crowded past 512 candidates: the radix passes), all-equal
     and short rows, with eligibility from q_pos, against the oracle."""
     rng = np.random.default_rng(23)
     R, stride = 1100, 5000
