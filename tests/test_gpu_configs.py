@@ -1,7 +1,8 @@
 """The five workloads at full size, in the launch configuration the benchmark times,
-against the CPU oracle on sampled rows (the oracle computes them one by one), plus
-properties checked on every row.  The Ascend page's long-prefill shape (7,810 queries
-on a 65,536-token cache, (24,2) heads) is an extra extend case."""
+against the CPU oracle on sampled rows (the oracle computes them one by one; every
+row of the extend chunk C4), plus properties checked on every row.  The Ascend
+page's long-prefill shape (7,810 queries on a 65,536-token cache, (24,2) heads) is
+an extra extend case, checked on every row as well."""
 import numpy as np
 import pytest
 import torch
@@ -144,15 +145,14 @@ def extend_full(case, sample):
     torch.cuda.synchronize()
     sel, cnt, out, lse = to_np(buf.sel_idx), to_np(buf.sel_cnt), to_np(buf.out), to_np(buf.lse)
     all_row_properties(case, sel, cnt, out, lse)
-    log(f"{case.name}: oracle on {len(sample)} sampled rows")
+    log(f"{case.name}: oracle on {len(sample)} of {case.R} rows")
     compare_rows(case, sample, sel, cnt, out, lse, stride)
 
 
-def test_c4_extend_full_sampled():
+def test_c4_extend_all_rows():
+    """All 4,096 rows of the extend chunk against the oracle."""
     case = synth.config("C4")
-    rng = np.random.default_rng(4)
-    sample = sorted(set([0, 1, 2, 3, 4095] + rng.choice(4096, 27, replace=False).tolist()))
-    extend_full(case, sample)
+    extend_full(case, list(range(case.R)))
 
 
 def test_c4_extend_shuffled_pages_sampled():
@@ -163,11 +163,12 @@ def test_c4_extend_shuffled_pages_sampled():
 
 
 def test_long_prefill_shape_of_the_ascend_tests():
-    """7,810 query rows appended to a cache totalling 65,536 tokens, (24,2) heads."""
+    """7,810 query rows appended to a cache totalling 65,536 tokens, (24,2) heads; every
+    row against the oracle, as the Ascend page's own test did on sampled rows."""
     total, new = 65536, 7810
     q_seq, q_pos = synth.extend_rows(total, new)
     case = synth.make_case("prefill7810", 7810, 24, 2, [total], page_size=64, q_seq=q_seq, q_pos=q_pos)
-    extend_full(case, [0, 1, 3905, 7808, 7809])
+    extend_full(case, list(range(case.R)))
 
 
 def test_longest_sequence_decode():
