@@ -312,16 +312,15 @@ def test_split_partials_merge_and_unsplit(S):
         np.testing.assert_allclose(ref.out[r], ref1.out[r], atol=1e-12)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
-def test_splits_without_tokens(kv_dtype):
-    """16 splits over sequences of 1 to 33 tokens (1 to 9 blocks selected): most
-    splits hold no token, and their partials must be 0 with lse -inf, as the oracle
-    gives.  The merged partials and the library's internal 16-way split must still
-    equal the oracle."""
+@pytest.mark.parametrize("kv_dtype,S", [("bf16", 16), ("fp8", 16), ("bf16", 64)])
+def test_splits_without_tokens(kv_dtype, S):
+    """16 or 64 (the most allowed) splits over sequences of 1 to 33 tokens (1 to 9
+    blocks selected): most splits hold no token, and their partials must be 0 with
+    lse -inf, as the oracle gives.  The merged partials and the library's internal
+    S-way split must still equal the oracle."""
     import block_sparse_attention_compress_amd as qsa
-    S = 16
-    case = small_decode(f"s16{kv_dtype}", 77, 16, 2, [1, 5, 9, 33], 64, jitter=True, kv_dtype=kv_dtype)
-    log(f"16 splits, few tokens, {kv_dtype} cache")
+    case = small_decode(f"s{S}{kv_dtype}", 77, 16, 2, [1, 5, 9, 33], 64, jitter=True, kv_dtype=kv_dtype)
+    log(f"{S} splits, few tokens, {kv_dtype} cache")
     d = Dev(case)
     d.compress()
     sc = d.scores()
