@@ -212,6 +212,26 @@ def test_selection_widths(L, k):
     check_decode_against_oracle(case, *res, k)
 
 
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_largest_k(num_splits):
+    """k = 2048, the most allowed: 8,192 selected tokens per (row, KV head), the
+    largest slot table and token loop, with the library's splits, one split and 5;
+    a 300-token row selects all of its 75 blocks."""
+    case = small_decode(f"k2048s{num_splits}", 88 + num_splits, 16, 2, [10000, 9001, 300], 64, topk=2048,
+                        jitter=True)
+    log(f"k=2048 splits={num_splits}")
+    res = run_decode(case, k=2048, num_splits=num_splits)
+    check_decode_against_oracle(case, *res, 2048)
+
+
+def test_largest_k_extend():
+    total, nq = 12000, 65
+    q_seq, q_pos = synth.extend_rows(total, nq)
+    case = synth.make_case("k2048ext", 89, 12, 1, [total], page_size=64, q_seq=q_seq, q_pos=q_pos, topk=2048)
+    res = run_extend(case, k=2048)
+    check_decode_against_oracle(case, *res, 2048)
+
+
 def test_zero_k_gives_zero_output_and_neg_inf_lse():
     case = small_decode("k0", 5, 16, 2, [1000, 77], 64, topk=0)
     d, sc, sel, cnt, out, lse = run_decode(case, k=0)
