@@ -79,6 +79,14 @@ def test_fused_selection_widths(L, k):
     check_fused(case, k=k)
 
 
+def test_fused_largest_k():
+    """k = 2048, the most allowed: the fused selection's lists and the attention's
+    8,192-token loop at their largest."""
+    case = small_decode("fk2048", 90, 16, 2, [10000, 9001, 300], 64, topk=2048, jitter=True)
+    log("fused k=2048")
+    check_fused(case, k=2048)
+
+
 @pytest.mark.parametrize("page_size", [4, 16, 256, 16384])
 def test_fused_page_sizes(page_size):
     lens = [16384, 5000, 777] if page_size == 16384 else [7000, 5000, 777]
