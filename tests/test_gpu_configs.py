@@ -206,3 +206,25 @@ def test_large_batch_decode():
     sel, cnt, out, lse = to_np(buf.sel_idx), to_np(buf.sel_cnt), to_np(buf.out), to_np(buf.lse)
     all_row_properties(case, sel, cnt, out, lse)
     compare_rows(case, [0, 1, 511, 777, 1023], sel, cnt, out, lse, stride)
+
+
+def test_most_rows_per_call():
+    """65,535 query rows, the most one call takes, on one 4,096-token sequence at
+    random positions, (12,1) heads: block scores, selection and attention, with
+    properties on every row and the oracle on sampled rows."""
+    rng = np.random.default_rng(65535)
+    R, L = 65535, 4096
+    q_seq = np.zeros(R, dtype=np.int32)
+    q_pos = rng.integers(0, L, size=R).astype(np.int32)
+    case = synth.make_case("rows65535", 65535, 12, 1, [L], page_size=64, q_seq=q_seq, q_pos=q_pos)
+    log(f"{case.name}: {R} rows on one {L}-token sequence")
+    dev, kv = upload(case)
+    qsa.qsa_compress_keys(kv)
+    stride = case.nb(0)
+    buf = ExtendBuffers.allocate(R, case.Hq, case.Hkv, stride, case.topk, "cuda")
+    extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, None, 0, scale=case.scale)
+    torch.cuda.synchronize()
+    sel, cnt, out, lse = to_np(buf.sel_idx), to_np(buf.sel_cnt), to_np(buf.out), to_np(buf.lse)
+    all_row_properties(case, sel, cnt, out, lse)
+    sample = sorted(set([0, 1, R - 2, R - 1] + rng.choice(R, 60, replace=False).tolist()))
+    compare_rows(case, sample, sel, cnt, out, lse, stride)
