@@ -1,12 +1,14 @@
-"""A decode step captured in a HIP graph replays to the same bits as the eager step,
-on several replays with eager work and synchronisations in between."""
+"""A decode step, and an extend chunk, captured in a HIP graph replay to the same
+bits as the eager calls, on several replays with eager work and synchronisations in
+between."""
 import numpy as np
 import pytest
 import torch
 
 import block_sparse_attention_compress_amd as qsa
 import synth
-from block_sparse_attention_compress_amd.pipeline import DecodeBuffers, DecodeGraph, decode_step
+from block_sparse_attention_compress_amd.pipeline import (DecodeBuffers, DecodeGraph, ExtendBuffers, decode_step,
+                                                         extend_step)
 from gpu_harness import log
 
 pytestmark = pytest.mark.gpu
@@ -55,3 +57,48 @@ def test_graph_replays_match_eager(num_splits, L_range):
     decode_step(kv, dev["q"], dev["q_pos"], buf, scale=case.scale, num_splits=num_splits)
     torch.cuda.synchronize()
     assert torch.equal(got, buf.out)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_extend_chunk_graph_replays_match_eager(kv_dtype):
+    """The extend chunk's four calls (block keys of the new tokens, tiled block
+    scores, many-row top-k, extend attention) in one captured graph."""
+    total, new = 6000, 1100   # 1,100 rows: the many-row top-k
+    q_seq, q_pos = synth.extend_rows(total, new)
+    case = synth.make_case(f"xgraph{kv_dtype}", 61, 12, 1, [total], page_size=64, q_seq=q_seq, q_pos=q_pos,
+                           jitter=True, kv_dtype=kv_dtype)
+    log(f"extend graph replay, {kv_dtype} cache")
+    dev = synth.to_device(case, "cuda")
+    kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
+    qsa.qsa_compress_keys(kv)
+    first = torch.tensor([total - new], dtype=torch.int32, device="cuda")
+    stride = case.nb(0)
+    buf = ExtendBuffers.allocate(case.R, case.Hq, case.Hkv, stride, case.topk, "cuda")
+
+    def chunk():
+        extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, first, new, scale=case.scale)
+
+    chunk()
+    torch.cuda.synchronize()
+    want = (buf.sel_idx.clone(), buf.sel_cnt.clone(), buf.out.clone(), buf.lse.clone(), dev["ckey"].clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chunk()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chunk()
+    for rep in range(4):
+        buf.out.fill_(float("nan"))
+        buf.lse.fill_(float("nan"))
+        buf.sel_idx.fill_(-9)
+        buf.scores.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (buf.sel_idx, buf.sel_cnt, buf.out, buf.lse, dev["ckey"])
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+        chunk()  # eager work between replays
+        torch.cuda.synchronize()
