@@ -125,6 +125,30 @@ def test_topk_rejects():
     assert status(L, P, 100, None, 2, 0, 16, P, P, None) == qsa.QSA_ERR_INVALID_ARG
 
 
+def test_last_error_is_per_thread():
+    """qsa_last_error() belongs to the calling thread: another thread's failure
+    does not show in it, and a thread that made no failed call reads ""."""
+    import threading
+    L = qsa.lib()
+    seen = {}
+
+    def fail_here():
+        seen["rc"] = L.qsa_topk_blocks(P, 100, None, 2, 2, 2049, P, P, None)
+        seen["msg"] = L.qsa_last_error().decode()
+
+    def look_only():
+        seen["other"] = L.qsa_last_error().decode()
+
+    t = threading.Thread(target=fail_here)
+    t.start()
+    t.join()
+    t = threading.Thread(target=look_only)
+    t.start()
+    t.join()
+    assert seen["rc"] == qsa.QSA_ERR_INVALID_ARG and "2049" in seen["msg"]
+    assert seen["other"] == ""
+
+
 def test_topk_ws_rejects_and_sizes():
     """The two-stage select: same argument checks as the one-stage call, plus the
     candidate workspace (two arrays of ceil(stride / 8192) * k entries per row and
