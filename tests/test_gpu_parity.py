@@ -399,6 +399,31 @@ def run_extend(case, k=None):
     return d, to_np(sc), to_np(sel), to_np(cnt), to_np(out), to_np(lse)
 
 
+def test_extend_strided_query_and_output_rows():
+    """Extend with q rows and out rows that are views into wider tensors (row
+    strides above Hq * 256): the scores, the selection and the outputs equal the
+    oracle's, and the columns past each row are not written."""
+    import block_sparse_attention_compress_amd as qsa
+    total, nq = 3000, 200
+    q_seq, q_pos = synth.extend_rows(total, nq)
+    case = synth.make_case("xstride", 515, 12, 1, [total], page_size=64, q_seq=q_seq, q_pos=q_pos)
+    d = Dev(case)
+    d.compress()
+    qbig = torch.zeros((case.R, case.Hq + 4, 256), dtype=torch.bfloat16, device="cuda")
+    qbig[:, :case.Hq] = d.t["q"]
+    qv = qbig[:, :case.Hq]
+    sc = d.scores(extend=True, q=qv)
+    sel, cnt = d.topk(sc, case.topk)
+    obig = torch.full((case.R, case.Hq + 3, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    ov = obig[:, :case.Hq]
+    lse = torch.full((case.R, case.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    qsa.qsa_sparse_attn_extend(d.kv, qv, qv.stride(0), d.t["q_seq"], d.t["q_pos"], case.R, case.Hq, sel, cnt,
+                               case.topk, 0.0, ov, ov.stride(0), lse)
+    torch.cuda.synchronize()
+    assert torch.all(obig[:, case.Hq:] == 7.0)
+    check_decode_against_oracle(case, d, to_np(sc), to_np(sel), to_np(cnt), to_np(ov), to_np(lse), case.topk)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(16, 2), (24, 2), (12, 1), (6, 1), (3, 1)])
 @pytest.mark.parametrize("nq", [1, 257])
 def test_extend_head_pairs(Hq, Hkv, nq):
