@@ -45,8 +45,8 @@ def log(msg: str):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extend", action="store_true", help="skip the extend (prefill chunk) figures")
