@@ -23,16 +23,20 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
                                                     uint16_t* __restrict__ out, float* __restrict__ out_lse) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
-    if (row >= N) return;
-    // the partials do not depend on the lse: their first batch is requested with it
+    if (row >= N) return;  // uniform per wave
+    // Every pass over the dims runs on all 64 lanes (a lane past D only skips its
+    // loads and stores), so the split weights broadcast from lanes 0..S-1 are
+    // always read from active lanes, whatever D is.
     const int d0 = 4 * lane;
     float4 o[kMergeBatch];
     auto load_batch = [&](int d, int sp0) {
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j)
-            if (sp0 + j < S && d < D)
-                o[j] = *reinterpret_cast<const float4*>(part_out + ((int64_t)(sp0 + j) * N + row) * D + d);
+            o[j] = (sp0 + j < S && d < D)
+                       ? *reinterpret_cast<const float4*>(part_out + ((int64_t)(sp0 + j) * N + row) * D + d)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
     };
+    // the partials do not depend on the lse: their first batch is requested with it
     load_batch(d0, 0);
     const float ls = lane < S ? part_lse[(int64_t)lane * N + row] : -INFINITY;
     const float M = wave_max(ls);
@@ -45,13 +49,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     const float w = lane < S ? expf(ls - M) : 0.f;
     const float z = wave_sum(w);
     const float wn = w / z;
-    for (int d = d0; d < D; d += 256) {
+    for (int db = 0; db < D; db += 256) {
+        const int d = db + d0;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int sp0 = 0; sp0 < S; sp0 += kMergeBatch) {
-            if (sp0 > 0 || d > d0) load_batch(d, sp0);
+            if (sp0 > 0 || db > 0) load_batch(d, sp0);
 #pragma unroll
             for (int j = 0; j < kMergeBatch; ++j) {
-                if (sp0 + j >= S) break;
+                if (sp0 + j >= S) break;  // uniform
                 const float ws = __shfl(wn, sp0 + j);
                 acc.x += ws * o[j].x;
                 acc.y += ws * o[j].y;
@@ -59,7 +64,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
                 acc.w += ws * o[j].w;
             }
         }
-        *reinterpret_cast<uint2*>(out + row * D + d) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+        if (d < D)
+            *reinterpret_cast<uint2*>(out + row * D + d) =
+                make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
     }
     if (lane == 0 && out_lse) out_lse[row] = M + logf(z);
 }

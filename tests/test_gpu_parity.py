@@ -386,6 +386,29 @@ def test_merge_kernel_against_oracle_with_empty_partials():
     assert np.all(to_np(out)[20] == 0)
 
 
+@pytest.mark.parametrize("D", [4, 64, 260, 1000])
+@pytest.mark.parametrize("S", [2, 17, 64])
+def test_merge_kernel_any_width_and_split_count(S, D):
+    """Widths that are not a multiple of 256 leave some lanes without dims on the
+    last pass; split counts above 16 take several load batches.  Every output must
+    still be the oracle's merge."""
+    import block_sparse_attention_compress_amd as qsa
+    rng = np.random.default_rng(1000 * S + D)
+    N = 9
+    po = rng.standard_normal((S, N, D)).astype(np.float32)
+    pl = (rng.standard_normal((S, N)) * 3).astype(np.float32)
+    pl[S - 1, 2] = -np.inf              # an empty last split
+    pl[:, 5] = -np.inf                  # a row with no tokens at all
+    po[:, 5] = 0
+    out = torch.full((N, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    qsa.qsa_merge_lse(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), S, N, D, out, lse)
+    ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64))
+    check_close(to_np(out), ro, f"merge out S={S} D={D}")
+    check_lse(to_np(lse), rl, f"merge lse S={S} D={D}")
+    assert np.all(to_np(out)[5] == 0)
+
+
 # ------------------------------------------------------------------- extend
 
 def run_extend(case, k=None):
