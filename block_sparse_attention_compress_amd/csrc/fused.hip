@@ -25,10 +25,18 @@
 // unit is still being scored holds a workgroup slot idle, and interleaving them
 // (attention of unit u after the scans of unit u + D) measured slower for every
 // lag D tried.  A waiting item only waits for items with lower tickets, which
-// running workgroups hold, so the wait always ends; it is still bounded (a
-// time-out is counted in the workspace and the item goes on).  Every counter and
-// flag is returned to zero by its last user, so the workspace needs no clearing
-// between calls.
+// running workgroups hold, so the wait always ends.  It is still bounded: an item
+// whose wait times out counts it in the workspace and writes a NaN partial in
+// place of its split, so the unit's output and lse come out NaN rather than
+// computed from a selection that may not be there yet.
+//
+// Flags carry the call's epoch instead of 0 / 1: the workspace holds a call
+// counter E, a unit's selection raises its ready word to E + 1, and attention
+// items wait for exactly that value.  A ready word left by an earlier call (even
+// one raised late, after a time-out) holds at most E and never satisfies a later
+// wait.  The arrival counters and the ticket counters are returned to zero by
+// their last user, and the last workgroup out advances E, so the workspace needs
+// no clearing between calls.
 //
 // Top-k of a unit (256 threads, scores read back from memory): an LDS histogram
 // of the top 12 bits of the order-preserving keys gives the bin B holding the
@@ -44,6 +52,8 @@
 // scores_stream_kernel, one 256-thread top-k takes some 30 us, and the last
 // unit's top-k, attention and merge form a tail that the separate calls do not
 // have.  It is kept as a correct single-launch alternative.
+#include <stdlib.h>
+
 #include "attn_body.h"
 #include "block_ops.h"
 #include "qsa_device.h"
@@ -80,11 +90,10 @@ struct FusedParams {
     uint16_t* out;
     int64_t out_stride;
     float* lse;
-    int* ctl;  // [0] ticket, [1] workgroups finished, [2] abandoned waits
-    int* scan_arrive;
-    int* ready;
-    int* att_arrive;
+    int* ctl;  // [0] ticket, [1] workgroups finished, [2] abandoned waits, [3] call epoch
+    int* unit_ctl;  // per unit, 4 ints: scan arrivals, ready word (epoch + 1), attention arrivals, unused
     int U, C, S, n_items;
+    int spin_limit;  // polls of a ready word before the wait is abandoned
 };
 
 // Item i -> (scan?, unit, chunk or split): the U C scan items first, unit by
@@ -423,7 +432,8 @@ __device__ __forceinline__ void select_unit(const float* __restrict__ s, int n, 
 // ---------------------------------------------------------------- merge
 
 // out / lse of the g heads of (row, KV head h) from the S partials (natural-log
-// lse; all -inf gives 0 and -inf), 4 dims per thread.
+// lse; all -inf gives 0 and -inf; a NaN partial, left by an abandoned wait, makes
+// the result NaN), 4 dims per thread.
 __device__ __forceinline__ void merge_unit(const FusedParams& F, int row, int h) {
     const AttnParams& A = F.A;
     const int g = A.g, S = A.S;
@@ -431,7 +441,10 @@ __device__ __forceinline__ void merge_unit(const FusedParams& F, int row, int h)
         const int head = h * g + (e >> 6);
         const int d = 4 * (e & 63);
         float M = -INFINITY;
-        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, A.part_lse[((int64_t)sp * A.R + row) * A.Hq + head]);
+        for (int sp = 0; sp < S; ++sp) {
+            const float x = A.part_lse[((int64_t)sp * A.R + row) * A.Hq + head];
+            M = (x != x || M != M) ? __builtin_nanf("") : fmaxf(M, x);
+        }
         uint16_t* o = F.out + (int64_t)row * F.out_stride + (int64_t)head * kHeadDim + d;
         if (M == -INFINITY) {
             *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
@@ -466,6 +479,10 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
     const int lane = tid & 63;
     const int wave = wave_id();
 
+    // the call's epoch: only the last workgroup out changes it, after every
+    // workgroup of the launch has passed this read
+    const int epoch = F.ctl[3];
+    const int raised = (int)((unsigned)epoch + 1u);  // a unit's ready word once its selection is written
     int next = 0;  // thread 0: the ticket claimed for the following item
     if (tid == 0) next = atomicAdd(&F.ctl[0], 1);
     for (;;) {
@@ -483,6 +500,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
         const int L = F.seq_lens[row];
         const int n_elig = L <= 0 ? 0 : min((L - 1) / 4 + 1, F.score_stride);
         float* srow = F.scores + (int64_t)u * F.score_stride;
+        int* uc = F.unit_ctl + 4 * (int64_t)u;  // scan arrivals, ready word, attention arrivals
 
         if (scan) {
             const int nch = max(1, (n_elig + kStreamChunk - 1) / kStreamChunk);
@@ -500,51 +518,66 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (tid == 0) {
-                const bool last = __hip_atomic_fetch_add(&F.scan_arrive[u], 1, __ATOMIC_RELAXED,
+                const bool last = __hip_atomic_fetch_add(&uc[0], 1, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT) == nch - 1;
                 if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 sh_last = last;
             }
             __syncthreads();
             if (!sh_last) continue;
-            if (tid == 0) F.scan_arrive[u] = 0;
+            if (tid == 0) uc[0] = 0;
             select_unit(srow, n_elig, F.k, F.sel_idx + (int64_t)u * F.k, F.sel_cnt + u, reinterpret_cast<int*>(smem));
             __syncthreads();
-            if (tid == 0) __hip_atomic_store(&F.ready[u], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) __hip_atomic_store(&uc[1], raised, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             if (tid == 0) {
                 int polls = 0;
-                while (__hip_atomic_load(&F.ready[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                bool ok = true;
+                while (__hip_atomic_load(&uc[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != raised) {
                     __builtin_amdgcn_s_sleep(8);
-                    if (++polls == kSpinLimit) {
+                    if (++polls >= F.spin_limit) {
                         atomicAdd(&F.ctl[2], 1);
+                        ok = false;
                         break;
                     }
                 }
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                sh_last = ok;
             }
             __syncthreads();
-            attend_split<KV8>(F.A, row, h, j, smem);
+            if (sh_last) {
+                attend_split<KV8>(F.A, row, h, j, smem);
+            } else {
+                // abandoned wait: the selection may not be written yet, so this split
+                // reports NaN, which the merge carries into the unit's output and lse
+                const AttnParams& A = F.A;
+                for (int e = tid; e < A.g * 64; e += kFusedThreads) {
+                    const int64_t prow = ((int64_t)j * A.R + row) * A.Hq + h * A.g + (e >> 6);
+                    const float nan = __builtin_nanf("");
+                    *reinterpret_cast<float4*>(A.part_out + prow * kHeadDim + 4 * (e & 63)) =
+                        make_float4(nan, nan, nan, nan);
+                    if ((e & 63) == 0) A.part_lse[prow] = nan;
+                }
+            }
             __syncthreads();
             if (tid == 0) {
-                const bool last = __hip_atomic_fetch_add(&F.att_arrive[u], 1, __ATOMIC_RELEASE,
+                const bool last = __hip_atomic_fetch_add(&uc[2], 1, __ATOMIC_RELEASE,
                                                          __HIP_MEMORY_SCOPE_AGENT) == F.S - 1;
                 if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 sh_last = last;
             }
             __syncthreads();
             if (!sh_last) continue;
-            if (tid == 0) {
-                F.att_arrive[u] = 0;
-                F.ready[u] = 0;
-            }
+            if (tid == 0) uc[2] = 0;
             merge_unit(F, row, h);
         }
     }
-    // the last workgroup out returns the ticket counters to zero for the next call
+    // the last workgroup out returns the ticket counters to zero and advances the
+    // epoch for the next call
     if (tid == 0 && atomicAdd(&F.ctl[1], 1) == (int)gridDim.x - 1) {
         F.ctl[0] = 0;
         F.ctl[1] = 0;
+        F.ctl[3] = raised;
     }
 }
 
@@ -566,7 +599,7 @@ FusedLayout fused_layout(int batch, int Hkv, int Hq, int max_seq_len, int S) {
     if (l.score_stride == 0) l.score_stride = 64;
     l.ctl = 0;
     l.arrive = 256;
-    l.scores = align256(l.arrive + (size_t)3 * U * sizeof(int));
+    l.scores = align256(l.arrive + (size_t)4 * U * sizeof(int));
     l.part_out = align256(l.scores + (size_t)U * l.score_stride * sizeof(float));
     l.part_lse = align256(l.part_out + (size_t)S * batch * Hq * kHeadDim * sizeof(float));
     l.total = align256(l.part_lse + (size_t)S * batch * Hq * sizeof(float));
@@ -590,7 +623,7 @@ size_t fused_workspace_bytes(int batch, int Hkv, int Hq, int max_seq_len, int S)
     return fused_layout(batch, Hkv, Hq, max_seq_len, S).total;
 }
 
-size_t fused_control_bytes(int batch, int Hkv) { return align256(256 + (size_t)3 * batch * Hkv * sizeof(int)); }
+size_t fused_control_bytes(int batch, int Hkv) { return align256(256 + (size_t)4 * batch * Hkv * sizeof(int)); }
 
 hipError_t launch_fused_decode(const PagedKV& kv, const Rows& rows, int k, float scale, int S, int32_t* sel_idx,
                                int32_t* sel_cnt, uint16_t* out, int64_t out_stride, float* lse, void* workspace,
@@ -646,13 +679,18 @@ hipError_t launch_fused_decode(const PagedKV& kv, const Rows& rows, int k, float
     F.out_stride = out_stride;
     F.lse = lse;
     F.ctl = reinterpret_cast<int*>(ws + l.ctl);
-    F.scan_arrive = reinterpret_cast<int*>(ws + l.arrive);
-    F.ready = F.scan_arrive + U;
-    F.att_arrive = F.ready + U;
+    F.unit_ctl = reinterpret_cast<int*>(ws + l.arrive);
     F.U = U;
     F.C = (l.score_stride + kStreamChunk - 1) / kStreamChunk;
     F.S = S;
     F.n_items = U * (F.C + S);
+    // QSA_FUSED_SPIN_LIMIT (tests of the time-out path only) shortens the bounded
+    // wait so that abandoned waits can be provoked without a stalled device
+    F.spin_limit = kSpinLimit;
+    if (const char* env = getenv("QSA_FUSED_SPIN_LIMIT")) {
+        const long v = strtol(env, nullptr, 10);
+        if (v >= 1 && v < kSpinLimit) F.spin_limit = (int)v;
+    }
 
     const size_t attn_loop = (size_t)A.table_words * 4 + attn_tile_bytes(kv.kv_fp8 != 0);
     const size_t attn_xchg = (size_t)kAttnWaves * A.g * kHeadDim * sizeof(float);

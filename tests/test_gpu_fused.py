@@ -23,9 +23,17 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def control_bytes(units: int) -> int:
-    # ticket words (256 B), then three int32 counters per (sequence, KV head)
-    return ((256 + 12 * units + 255) // 256) * 256
+def check_control(ws: torch.Tensor, units: int, calls_before: int):
+    """The control area after a call: ticket, finished and abandoned-wait counters
+    zero, the call counter advanced by one, every unit's arrival counters zero and
+    its ready word holding the number of this call."""
+    ctl = ws[:256].view(torch.int32).cpu().numpy()
+    assert ctl[0] == 0 and ctl[1] == 0, f"ticket counters not returned to zero: {ctl[:4]}"
+    assert ctl[2] == 0, "a wait was abandoned"
+    assert ctl[3] == calls_before + 1, f"call counter {ctl[3]}, expected {calls_before + 1}"
+    unit = ws[256:256 + 16 * units].view(torch.int32).cpu().numpy().reshape(units, 4)
+    assert np.all(unit[:, 0] == 0) and np.all(unit[:, 2] == 0), "arrival counters not returned to zero"
+    assert np.all(unit[:, 1] == ctl[3]), "a unit's ready word was not raised by this call"
 
 
 def fused(d: Dev, k=None, num_splits=0, scale=0.0, ws=None):
@@ -41,11 +49,11 @@ def fused(d: Dev, k=None, num_splits=0, scale=0.0, ws=None):
     if ws is None:
         ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     assert ws.numel() >= wsb
+    calls_before = int(ws[12:16].view(torch.int32).item())
     qsa.qsa_decode_fused(d.kv, q, q.stride(0), c.Hq, k, scale, num_splits, sel, cnt, out, out.stride(0), lse,
                          workspace=ws, workspace_bytes=ws.numel())
     torch.cuda.synchronize()
-    ctl = ws[:control_bytes(c.B * c.Hkv)]
-    assert int(torch.count_nonzero(ctl)) == 0, "control area not returned to zero"
+    check_control(ws, c.B * c.Hkv, calls_before)
     return to_np(sel), to_np(cnt), to_np(out), to_np(lse)
 
 
@@ -137,8 +145,10 @@ def test_fused_ties_resolved_in_lds_and_in_memory():
 
 
 def test_fused_workspace_reused_by_a_smaller_call():
-    """Two calls on one workspace, the second with fewer sequences: both correct, and
-    the control area is zero after each (checked inside fused())."""
+    """Three calls on one workspace, the second with fewer sequences: all correct, and
+    the control area consistent after each (checked inside fused()): the smaller
+    call leaves the larger call's later units untouched, and the third call's waits
+    are not satisfied by ready words of the earlier calls."""
     big = small_decode("fbig", 12, 16, 2, [9000, 7000, 5000, 3000], 64)
     small = small_decode("fsmall", 13, 16, 2, [4000, 2500], 64)
     dbig, dsmall = Dev(big), Dev(small)
@@ -152,7 +162,6 @@ def test_fused_workspace_reused_by_a_smaller_call():
         fsel, fcnt, fout, flse = fused(d, ws=ws)
         assert np.array_equal(fsel, to_np(sel_ref)) and np.array_equal(fcnt, to_np(cnt_ref))
         check_decode_against_oracle(d.case, d, to_np(sc), fsel, fcnt, fout, flse, d.case.topk)
-    assert int(ws[8:12].view(torch.int32).item()) == 0, "a wait was abandoned"
 
 
 def test_fused_matches_separate_path_at_full_size():
@@ -203,5 +212,74 @@ def test_fused_pipeline_step_and_graph_replay():
         assert torch.equal(buf.sel_idx, eager[2]), i
         assert torch.equal(buf.out, eager[0]), i
         assert torch.equal(buf.lse, eager[1]), i
-    ctl = buf.workspace[:control_bytes(case.B * case.Hkv)]
-    assert int(torch.count_nonzero(ctl)) == 0
+    # two eager calls and three replays on the workspace
+    check_control(buf.workspace, case.B * case.Hkv, 4)
+
+
+def test_fused_abandoned_wait_gives_nan_and_leaves_no_stale_flag(monkeypatch):
+    """The bounded wait's time-out, forced from the host with a one-poll limit: a
+    unit whose selection was not ready when its attention item polled reports NaN
+    out and lse (never a result from a stale selection), the abandoned waits are
+    counted, and a later call on the same workspace with the normal limit is exact
+    again -- ready words raised late by the short-limit call do not satisfy it."""
+    case = small_decode("ftimeout", 15, 16, 2, [9000, 4097, 6000, 12000, 3000, 7000], 64)
+    d = Dev(case)
+    d.compress()
+    U = case.B * case.Hkv
+    ws = torch.zeros(qsa.qsa_decode_fused_workspace_bytes(d.kv, case.Hq, case.topk, 0), dtype=torch.uint8,
+                     device="cuda")
+    ref_sel, ref_cnt, ref_out, ref_lse = fused(d, ws=ws)            # normal limit: exact, checked in fused()
+    monkeypatch.setenv("QSA_FUSED_SPIN_LIMIT", "1")
+    q = d.t["q"]
+    nan_units = 0
+    for rep in range(3):
+        sel = torch.full((case.B, case.Hkv, case.topk), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((case.B, case.Hkv), -7, dtype=torch.int32, device="cuda")
+        out = torch.zeros((case.B, case.Hq, 256), dtype=torch.bfloat16, device="cuda")
+        lse = torch.zeros((case.B, case.Hq), dtype=torch.float32, device="cuda")
+        before = int(ws[8:12].view(torch.int32).item())
+        qsa.qsa_decode_fused(d.kv, q, q.stride(0), case.Hq, case.topk, 0.0, 0, sel, cnt, out, out.stride(0), lse,
+                             workspace=ws, workspace_bytes=ws.numel())
+        torch.cuda.synchronize()
+        abandoned = int(ws[8:12].view(torch.int32).item()) - before
+        o, l = to_np(out), to_np(lse)
+        nan_here = 0
+        for r in range(case.B):
+            for h in range(case.Hkv):
+                heads = slice(h * case.g, (h + 1) * case.g)
+                if np.isnan(l[r, heads]).any() or np.isnan(o[r, heads]).any():
+                    assert np.isnan(l[r, heads]).all() and np.isnan(o[r, heads]).all(), (rep, r, h)
+                    nan_here += 1
+                else:
+                    assert np.array_equal(o[r, heads], ref_out[r, heads]), (rep, r, h)
+                    assert np.array_equal(l[r, heads], ref_lse[r, heads]), (rep, r, h)
+        assert (abandoned > 0) == (nan_here > 0) and nan_here <= abandoned, (rep, abandoned, nan_here)
+        assert np.array_equal(to_np(sel), ref_sel) and np.array_equal(to_np(cnt), ref_cnt), rep
+        nan_units += nan_here
+    log(f"fused one-poll limit: {nan_units} of {3 * U} units reported NaN")
+    monkeypatch.delenv("QSA_FUSED_SPIN_LIMIT")
+    abandoned_total = int(ws[8:12].view(torch.int32).item())
+    sel, cnt, out, lse = fused_counted(d, ws)
+    assert int(ws[8:12].view(torch.int32).item()) == abandoned_total
+    assert np.array_equal(sel, ref_sel) and np.array_equal(cnt, ref_cnt)
+    assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse)
+
+
+def fused_counted(d: Dev, ws: torch.Tensor):
+    """One fused call on a workspace that may carry abandoned waits from earlier calls
+    (the abandoned-wait word is not reset): outputs and the rest of the control area."""
+    c = d.case
+    q = d.t["q"]
+    sel = torch.full((c.B, c.Hkv, c.topk), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((c.B, c.Hkv), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((c.B, c.Hq, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((c.B, c.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    calls_before = int(ws[12:16].view(torch.int32).item())
+    qsa.qsa_decode_fused(d.kv, q, q.stride(0), c.Hq, c.topk, 0.0, 0, sel, cnt, out, out.stride(0), lse,
+                         workspace=ws, workspace_bytes=ws.numel())
+    torch.cuda.synchronize()
+    ctl = ws[:16].view(torch.int32).cpu().numpy()
+    assert ctl[0] == 0 and ctl[1] == 0 and ctl[3] == calls_before + 1
+    unit = ws[256:256 + 16 * c.B * c.Hkv].view(torch.int32).cpu().numpy().reshape(-1, 4)
+    assert np.all(unit[:, 0] == 0) and np.all(unit[:, 2] == 0) and np.all(unit[:, 1] == ctl[3])
+    return to_np(sel), to_np(cnt), to_np(out), to_np(lse)
