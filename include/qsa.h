@@ -119,77 +119,81 @@ QSA_API int qsa_version(void);
 QSA_API const char* qsa_last_error(void);
 
 /*
- * a1 -- block keys.  For every sequence s and KV head h, and every block b
- * with 4b < L_s and 4b + 3 >= first_token[s] (first_token NULL = 0), writes
+ * a1 -- block keys.  Source: "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat de pull
+ * request daadwerkelijk verandert" (the indexer compresses the keys into microblocks at
+ * compression ratio 4). For every sequence s and KV head h, and every block b with 4b < L_s and
+ * 4b + 3 >= first_token[s] (first_token NULL = 0), writes
  *   ckey[b] = fp32 mean of the block's n = min(4, L_s - 4b) keys,
- * computed exactly as ((k0 + k1) + (k2 + k3)) * 0.25 for n = 4 and as the
- * left-to-right sum divided by n (correctly rounded) for n < 4 (bf16 and fp8
- * block keys: that mean rounded to nearest, ties to even; fp8 held at +-448).  The pages
- * say only that keys are compressed into 4-token microblocks; this pooling is
- * the stated reading.  Idempotent: a page shared by two sequences gets the
- * same values from both.  Decode calls it with first_token = L_s - 1 to
- * refresh the block holding the newest token; extend with the first new
- * position.  max_new_tokens is a host bound on L_s - first_token[s] used to
- * size the grid (<= 0: max_seq_len); it is ignored when first_token is NULL.
+ * computed exactly as ((k0 + k1) + (k2 + k3)) * 0.25 for n = 4 and as the left-to-right sum
+ * divided by n (correctly rounded) for n < 4 (bf16 and fp8 block keys: that mean rounded to
+ * nearest, ties to even; fp8 held at +-448).  The pages say only that keys are compressed into
+ * 4-token microblocks; this pooling is the stated reading.  Idempotent: a page shared by two
+ * sequences gets the same values from both.  Decode calls it with first_token = L_s - 1 to refresh
+ * the block holding the newest token; extend with the first new position.  max_new_tokens is a
+ * host bound on L_s - first_token[s] used to size the grid (<= 0: max_seq_len); it is ignored when
+ * first_token is NULL.
  */
 QSA_API int qsa_compress_keys(const qsa_kv_t* kv, const int32_t* first_token, int32_t max_new_tokens,
                               void* stream);
 
 /*
- * a2 -- block scores.  q: bf16 rows, row r at q + r * q_row_stride
- * (elements), heads contiguous inside a row ([Hq][256]).  q_seq / q_pos
- * (int32 [R]) give each row's sequence and position; both may be NULL for
- * decode (row r = sequence r at t = L_r - 1, R must equal batch).  Writes
+ * a2 -- block scores.  Source: "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat de
+ * pull request daadwerkelijk verandert" (the indexer scores the microblocks against the query). q:
+ * bf16 rows, row r at q + r * q_row_stride (elements), heads contiguous inside a row ([Hq][256]).
+ * q_seq / q_pos (int32 [R]) give each row's sequence and position; both may be NULL for decode
+ * (row r = sequence r at t = L_r - 1, R must equal batch).  Writes
  *   scores[(r * Hkv + h) * score_stride + b] = (sum_{j in group h} q[r][j]) . ckey[b]
- * in fp32 for b < n_elig(r) = min(t / 4 + 1, score_stride); entries at or
- * after n_elig(r) are not written.  The scale is not applied (it does not
- * change the order).  Rows sharing a sequence are scored with matrix cores
- * when there are more rows than sequences (extend).  R <= 65535 per call.
+ * in fp32 for b < n_elig(r) = min(t / 4 + 1, score_stride); entries at or after n_elig(r) are not
+ * written.  The scale is not applied (it does not change the order).  Rows sharing a sequence are
+ * scored with matrix cores when there are more rows than sequences (extend).  R <= 65535 per call.
  */
 QSA_API int qsa_block_scores(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
                      const int32_t* q_pos, int32_t R, int32_t Hq, float* scores, int32_t score_stride,
                      void* stream);
 
 /*
- * a1 + a2 for one decode step in one launch: the same results, bit for bit, as
+ * a1 + a2 for one decode step in one launch (source as for a1 and a2: "Qwen 4 QSA krijgt
+ * decode-contextparallellisme", section "Wat de pull request daadwerkelijk verandert"). The same
+ * results, bit for bit, as
  *   qsa_compress_keys(kv, first_token = {L_s - 1}, 1, stream);
  *   qsa_block_scores(kv, q, q_row_stride, NULL, NULL, batch, Hq, scores, score_stride, stream);
- * i.e. the block key holding each sequence's newest token is rebuilt from K (and
- * stored), and every eligible block of every row is scored, the newest one
- * with its rebuilt key.  Sequences with L_s = 0 are skipped.  The block keys
- * rebuilt here must not be read by another sequence of the same call (the page
- * holding a sequence's newest token belongs to that sequence alone, as in a
- * paged cache that copies a shared page before appending to it).  Arguments
- * and errors as for the two calls.
+ * i.e. the block key holding each sequence's newest token is rebuilt from K (and stored), and
+ * every eligible block of every row is scored, the newest one with its rebuilt key.  Sequences
+ * with L_s = 0 are skipped.  The block keys rebuilt here must not be read by another sequence of
+ * the same call (the page holding a sequence's newest token belongs to that sequence alone, as in
+ * a paged cache that copies a shared page before appending to it).  Arguments and errors as for
+ * the two calls.
  */
 QSA_API int qsa_decode_scores_refresh(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq,
                                       float* scores, int32_t score_stride, void* stream);
 
 /*
- * a3 -- top-k selection.  For each (row, KV head): among the n_elig(r)
- * scores (q_pos as above; NULL means n_elig = score_stride for every row),
- * keeps the k largest under the order (score descending, block index
- * ascending; -0 equals +0), and writes them in ascending block order to
+ * a3 -- top-k selection.  Source: "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat de
+ * pull request daadwerkelijk verandert" (the best 512 blocks, about 2,048 token positions, are
+ * kept); the -1 padding of a selection list is the one on "Qwen4-Exp QSA komt naar Huawei's
+ * Ascend", section "Wat de pull request daadwerkelijk toevoegt". For each (row, KV head): among
+ * the n_elig(r) scores (q_pos as above; NULL means n_elig = score_stride for every row), keeps the
+ * k largest under the order (score descending, block index ascending; -0 equals +0), and writes
+ * them in ascending block order to
  *   sel_idx[(r * Hkv + h) * k + j], j < cnt, then -1 up to k,
  *   sel_cnt[r * Hkv + h] = cnt = min(k, n_elig(r)).
- * 0 <= k <= QSA_MAX_TOPK.  Scores must be finite.  Rows are read with 16-byte
- * loads when score_stride is a multiple of 4 and scores is 16-byte aligned
- * (any stride works).
+ * 0 <= k <= QSA_MAX_TOPK.  Scores must be finite.  Rows are read with 16-byte loads when
+ * score_stride is a multiple of 4 and scores is 16-byte aligned (any stride works).
  */
 QSA_API int qsa_topk_blocks(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R, int32_t Hkv,
                     int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* stream);
 
 /*
- * a3, long rows -- the same selection as qsa_topk_blocks, bit for bit, for
- * rows longer than 16,384 blocks computed in two launches: every 8,192-block
- * slice of a row keeps its own top k (so one row spreads over many compute
- * units), then the top k of those candidates is taken.  The candidates live in
- * `workspace` (device memory, 16-byte aligned, caller-owned, contents on entry
- * ignored and on return unspecified), which must hold
- * qsa_topk_workspace_bytes(R, Hkv, k, score_stride) bytes; when that is 0 the
- * call is qsa_topk_blocks and workspace may be NULL.  Arguments and errors as
- * qsa_topk_blocks, plus QSA_ERR_INVALID_ARG for a missing, short or misaligned
- * workspace.  Calls sharing one workspace must be ordered on one stream.
+ * a3, long rows (source as for a3: "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat
+ * de pull request daadwerkelijk verandert"). The same selection as qsa_topk_blocks, bit for bit,
+ * for rows longer than 16,384 blocks computed in two launches: every 8,192-block slice of a row
+ * keeps its own top k (so one row spreads over many compute units), then the top k of those
+ * candidates is taken.  The candidates live in `workspace` (device memory, 16-byte aligned,
+ * caller-owned, contents on entry ignored and on return unspecified), which must hold
+ * qsa_topk_workspace_bytes(R, Hkv, k, score_stride) bytes; when that is 0 the call is
+ * qsa_topk_blocks and workspace may be NULL.  Arguments and errors as qsa_topk_blocks, plus
+ * QSA_ERR_INVALID_ARG for a missing, short or misaligned workspace.  Calls sharing one workspace
+ * must be ordered on one stream.
  */
 QSA_API int qsa_topk_blocks_ws(const float* scores, int32_t score_stride, const int32_t* q_pos, int32_t R,
                                int32_t Hkv, int32_t k, int32_t* sel_idx, int32_t* sel_cnt, void* workspace,
@@ -200,13 +204,21 @@ QSA_API int qsa_topk_blocks_ws(const float* scores, int32_t score_stride, const 
 QSA_API size_t qsa_topk_workspace_bytes(int32_t R, int32_t Hkv, int32_t k, int32_t score_stride);
 
 /*
- * a4 -- sparse attention, decode (one row per sequence at t = L_s - 1).
- * sel_idx / sel_cnt as written by qsa_topk_blocks ([batch][Hkv][k], ascending,
- * every block eligible).  For query head j of KV head h the token set is
+ * a4 -- sparse attention, decode (one row per sequence at t = L_s - 1). Source: "Qwen 4 QSA krijgt
+ * decode-contextparallellisme", section "Wat de pull request daadwerkelijk verandert" (softmax and
+ * value sum run over the uncompressed K and V of the selected tokens; the split read whose partial
+ * results are combined at the end), and "Qwen4-Exp QSA komt naar Huawei's Ascend", section "Wat de
+ * pull request daadwerkelijk toevoegt" (head dimension 256 in bf16, the original 1/sqrt(256)
+ * scale, zero output for fully masked rows). sel_idx / sel_cnt as written by qsa_topk_blocks
+ * ([batch][Hkv][k], ascending, every block eligible).  For query head j of KV head h the token set
+ * is
  *   T = { 4b + u : b selected, 0 <= u < 4, 4b + u < L_s }
- * and the result is softmax(scale * q_j . K_T^T) . V_T with an fp32 online
- * softmax; scale <= 0 selects 1/sqrt(256) = 1/16.  An empty T gives output 0
- * and lse = -inf (fully masked rows keep a zero output, as on the Ascend page).
+ * and the result is softmax(scale * q_j . K_T^T) . V_T; scale <= 0 selects 1/sqrt(256) = 1/16.
+ * Arithmetic: the g query heads of a KV head form one 16-row bf16 matrix-core tile; q . K^T
+ * accumulates in fp32, the online softmax (running max and normaliser) is fp32, the weights P are
+ * rounded to bf16 for the P . V product (fp32 accumulation), and the normaliser sums the rounded
+ * weights.  An empty T gives output 0 and lse = -inf (fully masked rows keep a zero output, as on
+ * the Ascend page).
  *
  * Split-KV: the selected tokens, in order, have ranks p = 0..|T|-1.
  *  - part_out != NULL: num_splits = S >= 1 partials are written, split s
@@ -231,11 +243,12 @@ QSA_API int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_
 QSA_API size_t qsa_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t num_splits);
 
 /*
- * Fused decode: a2 + a3 + a4 + a5 of one decode step in a single launch -- the
- * same block scores, the same top-k order and selection, and the same split
- * attention and log-sum-exp merge as the separate calls above, with the steps
- * of different (sequence, KV head) units overlapping.  Block keys must be
- * current (qsa_compress_keys first, as for qsa_block_scores).
+ * Fused decode (source as for a2-a5: "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat
+ * de pull request daadwerkelijk verandert"). a2 + a3 + a4 + a5 of one decode step in a single
+ * launch -- the same block scores, the same top-k order and selection, and the same split
+ * attention and log-sum-exp merge as the separate calls above, with the steps of different
+ * (sequence, KV head) units overlapping.  Block keys must be current (qsa_compress_keys first, as
+ * for qsa_block_scores).
  *   sel_idx int32 [batch][Hkv][k] and sel_cnt int32 [batch][Hkv] receive the
  *     selection, exactly as qsa_topk_blocks writes it;
  *   out bf16 at out + row * out_row_stride ([Hq][256] per row, 8-byte aligned,
@@ -243,14 +256,17 @@ QSA_API size_t qsa_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t num
  *     the result, as qsa_sparse_attn_decode writes it;
  *   num_splits: attention splits per (sequence, KV head), 0 = the library's
  *     choice; the result does not depend on it beyond rounding.
- * workspace: qsa_decode_fused_workspace_bytes(kv, Hq, k, num_splits) bytes,
- * 256-byte aligned.  It holds the scores, the partials and a control area of
- * counters and flags that must be all zero when the call starts: zero-fill the
- * workspace once before its first use; every call leaves the control area zero
- * again, so later calls need no clearing.  Calls that share a workspace must
- * not overlap (issue them on one stream).  The word at workspace + 8 (int32)
- * counts waits that were abandoned after about a second (0 unless the device
- * stalls); it is never reset by the library.
+ * workspace: qsa_decode_fused_workspace_bytes(kv, Hq, k, num_splits) bytes, 256-byte aligned. It
+ * holds the scores, the partials and a control area of counters and flags.  Zero-fill the
+ * workspace once before its first use; the library keeps the control area consistent from then
+ * on, so later calls need no clearing (a workspace may also serve a later call with fewer
+ * sequences).  After every call its ticket and arrival counters are zero again, the int32 word at
+ * workspace + 12 counts the calls made on the workspace, and each unit's ready word holds the
+ * number of the call that last raised it.  Calls that share a workspace must not overlap (issue
+ * them on one stream).  An attention item waits for its unit's selection for at most about a
+ * second (only a stalled device takes that long): when a wait is abandoned, the int32 word at
+ * workspace + 8 is incremented (it is never reset by the library) and that unit's out and lse
+ * rows are written as NaN, never as a result computed from a selection that may be stale.
  */
 QSA_API int qsa_decode_fused(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq, int32_t k,
                              float scale, int32_t num_splits, int32_t* sel_idx, int32_t* sel_cnt, void* out,
@@ -261,12 +277,16 @@ QSA_API int qsa_decode_fused(const qsa_kv_t* kv, const void* q, int64_t q_row_st
 QSA_API size_t qsa_decode_fused_workspace_bytes(const qsa_kv_t* kv, int32_t Hq, int32_t k, int32_t num_splits);
 
 /*
- * a6 -- sparse attention, extend.  Like decode, but every query row r has its
- * own sequence q_seq[r], position t = q_pos[r] and selection, and tokens
- * after t are masked: T = { 4b + u : b selected, 4b + u < L, 4b + u <= t }.
- * Writes out (bf16, row stride out_row_stride) and lse ([R][Hq], may be NULL).
- * The g heads of a KV head are padded to 16 matrix-core rows in the kernel;
- * the padded rows are discarded (the Ascend page pads 12 -> 16 for its tiler).
+ * a6 -- sparse attention, extend.  Source: "Qwen4-Exp QSA komt naar Huawei's Ascend", section "Wat
+ * de pull request daadwerkelijk toevoegt" (extend / prefill rows, bf16 head dimension 256, heads
+ * padded to a power of two with the padded outputs discarded, zero output for fully masked rows)
+ * and "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat de pull request daadwerkelijk
+ * verandert" (attention over the selected tokens' uncompressed K and V).  Like decode, but every
+ * query row r has its own sequence q_seq[r], position t = q_pos[r] and selection, and tokens after
+ * t are masked: T = { 4b + u : b selected, 4b + u < L, 4b + u <= t }. Writes out (bf16, row stride
+ * out_row_stride) and lse ([R][Hq], may be NULL). The g heads of a KV head are padded to 16
+ * matrix-core rows in the kernel; the padded rows are discarded (the Ascend page pads 12 -> 16 for
+ * its tiler).
  */
 QSA_API int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
                            const int32_t* q_pos, int32_t R, int32_t Hq, const int32_t* sel_idx,
@@ -274,13 +294,15 @@ QSA_API int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_
                            float* lse, void* stream);
 
 /*
- * a5 -- log-sum-exp merge of S partial results (the combine step of decode
- * context parallelism on the DCP page, section on how it differs from tensor
- * parallelism):  part_out fp32 [S][N][D], part_lse fp32 [S][N] ->
+ * a5 -- log-sum-exp merge of S partial results.  Source: "Qwen 4 QSA krijgt
+ * decode-contextparallellisme", section "Wat de pull request daadwerkelijk verandert" (the
+ * attention results of the split read are combined at the end) and its question "Hoe verschilt
+ * decode-contextparallellisme van tensorparallellisme?" (each rank reads its own slice, the
+ * partial results are merged):  part_out fp32 [S][N][D], part_lse fp32 [S][N] ->
  *   lse = M + ln sum_s exp(lse_s - M),  M = max_s lse_s,
  *   out = sum_s exp(lse_s - lse) * o_s   (bf16 [N][D]),
- * all partials -inf -> out 0, lse -inf.  1 <= S <= QSA_MAX_SPLITS,
- * D a multiple of 4 up to 1024.  out_lse may be NULL.
+ * all partials -inf -> out 0, lse -inf.  1 <= S <= QSA_MAX_SPLITS, D a multiple of 4 up to 1024.
+ * out_lse may be NULL.
  */
 QSA_API int qsa_merge_lse(const float* part_out, const float* part_lse, int32_t S, int32_t N, int32_t D, void* out_bf16,
                   float* out_lse, void* stream);
