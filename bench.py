@@ -7,15 +7,32 @@ against the group-summed query, keep the top-512 blocks, run the sparse attentio
 over their uncompressed K/V (split-KV partials merged by log-sum-exp).  Inputs are
 seeded synthetic tensors (``synth``) already resident in HBM when timing starts.
 
-Default workload: 32 sequences with lengths uniform on [32768, 65536], 16 query /
-2 KV heads, head_dim 256, bf16 K/V with a U(0.5, 2) norm jitter per token,
-64-token pages under a shuffled block table, top-512 blocks.
+Headline workload (``value``): 32 sequences with lengths uniform on
+[32768, 65536], 16 query / 2 KV heads, head_dim 256, bf16 K/V with a U(0.5, 2)
+norm jitter per token, 64-token pages under a shuffled block table, top-512
+blocks.  The default run also measures the other decode workloads, each with its
+own roofline and CPU oracle baseline, under ``configs``:
 
-Prints one JSON line: queries/s for the step, the roofline of the dominant kernel
-(the block-score scan over fp32 block keys, HBM-bound), and the CPU oracle timed
-on a bounded sample of the same workload on the host cores.
+* C1  1 sequence of 8192 tokens, (16,2) heads, one contiguous page;
+* C3  8 sequences of 262144 tokens, (24,2) heads, 1 % of the microblocks biased
+      toward the query, 64-token shuffled pages;
+* C5  64 sequences of 65536..131072 tokens, (6,1) heads, 64-token shuffled
+      pages, timed as configured -- 4 token-interleaved split partials merged by
+      ``qsa_merge_lse`` -- and beside it with the library's internal split;
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config C2]
+and the extend chunk (4096 new tokens on 28672 cached, (12,1) heads) under
+``extend``.
+
+Prints one JSON line.  Per workload: queries/s, ms per step, per-kernel HIP-event
+times, the roofline of the dominant kernel (the block-score scan, HBM-bound: the
+algorithmic bytes of that launch over its event time) with the step's
+own fraction beside it, and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.  Algorithmic bytes are what the method must move:
+the block-key scan, the selected tokens' K and V, q, out, lse, the block table
+and the lengths; scores, the rebuilt newest block key and split partials are the
+implementation's overhead and are reported apart.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config C2|C1|C3|C5|all]
     python bench.py --copy-calibration      # plain copy kernel for counter scaling
 """
 from __future__ import annotations
@@ -33,9 +50,11 @@ if ROOT not in sys.path:
 
 METRIC = "QSA decode queries/s and achieved HBM GB/s (% of MI355X peak) at 64K ctx"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scores_stream_kernel_C2_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 SCORES_SRC = [os.path.join(ROOT, "block_sparse_attention_compress_amd", "csrc", f)
               for f in ("scores.hip", "scan_body.h", "qsa_device.h")]
+DTYPE = "fp32 block-key scores; bf16 K/V on bf16 MFMA with fp32 accumulate (P rounded to bf16)"
+DECODE_CONFIGS = ("C2", "C1", "C3", "C5")
 
 
 def log(msg: str):
@@ -47,12 +66,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C5"])
+    p.add_argument("--config", default="all", choices=["all", "C1", "C2", "C3", "C5"],
+                   help="decode workload(s): all = C2 (headline) then C1, C3, C5")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extend", action="store_true", help="skip the extend (prefill chunk) figures")
     p.add_argument("--extend-only", action="store_true",
                    help="print only the extend chunk's figures (one JSON object; for profiling the chunk alone)")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle timing span (seconds of wall time)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="oracle timing span for the headline workload (seconds of wall time; the other "
+                        "workloads take 40 %% of it)")
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--graph", action="store_true", help="time a replayed HIP graph of the step instead of eager launches")
     p.add_argument("--splits", type=int, default=None, help="decode split count (default: the library's choice)")
@@ -83,7 +105,7 @@ def describe(case) -> str:
     if case.bias_frac:
         extra.append(f"{case.bias_frac:.0%} of microblocks biased +{case.bias_mag:g} sigma toward the query")
     if case.splits > 1:
-        extra.append(f"{case.splits} split-KV partitions merged by log-sum-exp")
+        extra.append(f"{case.splits} token-interleaved split-KV partials merged by log-sum-exp")
     if case.ckey_dtype == "bf16":
         extra.append("bf16 block keys (fp32 means rounded to nearest even)")
     if case.ckey_dtype == "fp8":
@@ -114,16 +136,18 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
-def decode_bytes(case, sel, cnt, page_size):
-    """Algorithmic HBM bytes of one decode step, and of its refresh-and-score launch.
+def decode_bytes(case, sel, cnt, page_size, splits):
+    """Algorithmic HBM bytes of one decode step and the implementation's
+    overhead bytes, for the step and for the block-score launch.
 
-    step: per (sequence, KV head) the block-key scan (nb * 1 KiB for fp32 keys,
-    nb * 512 B for bf16 keys, nb * 256 B for fp8 keys), the rebuilt newest block key (its 1..4 bf16 K rows
-    read, one block key written) and the bf16 K and V rows of the selected tokens
-    (512 B each), plus q and out rows (bf16), lse (fp32), the block table and the
-    lengths.
-    refresh-and-score launch: the block-key scan, the rebuilt key, the q rows,
-    the score writes (4 B per block) and the block table."""
+    Algorithmic, per (sequence, KV head): the block-key scan (nb * 1 KiB for fp32
+    keys, 512 B bf16, 256 B fp8) and the K and V rows of the selected tokens
+    (512 B each, 256 B for an fp8 cache); per row: q and out (bf16) and lse
+    (fp32); the block-table entries and the lengths.  The block-score launch's
+    share is the scan, q, the table and the lengths.
+    Overhead: the scores written by the scan and read back by the top-k (4 B per
+    block each way), the newest block key rebuilt in the scan (1..4 K rows read,
+    one key written) and the split partials (fp32 out + lse, written and read)."""
     import numpy as np
 
     B, Hkv, Hq = case.B, case.Hkv, case.Hq
@@ -131,7 +155,6 @@ def decode_bytes(case, sel, cnt, page_size):
     key_bytes = 256 * {"bf16": 2, "fp8": 1}.get(case.ckey_dtype, 4)
     ckey = int(nb.sum()) * Hkv * key_bytes
     row_bytes = 256 if case.kv_dtype == "fp8" else 512  # one K or V row
-    refresh = sum((int(L) - 4 * ((int(L) - 1) // 4)) * row_bytes + key_bytes for L in case.lens if L > 0) * Hkv
     tokens = 0
     for i in range(B):
         L = int(case.lens[i])
@@ -140,11 +163,16 @@ def decode_bytes(case, sel, cnt, page_size):
             blocks = sel[i, h, :c].astype(np.int64)
             tokens += int(np.minimum(L - 4 * blocks, 4).sum())
     kv_bytes = tokens * row_bytes * 2
-    qo = B * Hq * 256 * 2 * 2 + B * Hq * 4
+    q_bytes = B * Hq * 256 * 2
+    qo = q_bytes * 2 + B * Hq * 4
     table = int(sum((int(L) + page_size - 1) // page_size for L in case.lens)) * 4 + B * 4
-    step = ckey + refresh + kv_bytes + qo + table
-    scores = ckey + refresh + B * Hq * 256 * 2 + int(nb.sum()) * Hkv * 4 + table
-    return step, scores, tokens
+    step = ckey + kv_bytes + qo + table
+    scan = ckey + q_bytes + table
+    refresh = sum((int(L) - 4 * ((int(L) - 1) // 4)) * row_bytes + key_bytes for L in case.lens if L > 0) * Hkv
+    score_rw = int(nb.sum()) * Hkv * 4
+    partials = (splits * B * Hq * (256 + 1) * 4 * 2) if splits > 1 else 0
+    return {"step": step, "scan": scan, "tokens": tokens,
+            "scan_overhead": score_rw + refresh, "step_overhead": 2 * score_rw + refresh + partials}
 
 
 def cpu_model() -> str:
@@ -157,13 +185,14 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(case, target_s: float):
+def cpu_baseline(case, target_s: float, max_rows: int):
     """The CPU oracle as it stands, timed on a sample of the same workload: on
-    every host thread it may use, and on one thread (a shorter sample)."""
+    every host thread it may use (one (row, KV head) unit per thread), and on one
+    thread (a shorter sample)."""
     import oracle
 
     threads = oracle.default_threads()
-    rows = list(range(min(case.B, 8)))
+    rows = list(range(min(case.B, max_rows)))
     data = oracle.CaseData(case)
     data.prefetch([case.q_seq[r] for r in rows], threads)      # logical K and block keys: not timed
     for r in rows:
@@ -181,16 +210,233 @@ def cpu_baseline(case, target_s: float):
 
     reps, dt = timed(rows, threads, target_s)
     reps1, dt1 = timed(rows[:1], 1, max(1.0, target_s / 4))
-    return {"value": round(reps * len(rows) / dt, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 oracle decode step (scores, top-512, attention) on sequences 0..{len(rows) - 1} of "
-                      f"the {case.B}-sequence workload, {reps} repetitions in {dt:.2f} s, block keys precomputed",
+    used = min(threads, len(rows) * case.Hkv)
+    return {"value": round(reps * len(rows) / dt, 3), "unit": "queries/s", "cores": used, "kind": "oracle",
+            "sample": f"fp64 oracle decode step (scores, top-{case.topk}, attention"
+                      f"{', 4 interleaved splits merged' if case.splits > 1 else ''}) on sequences "
+                      f"0..{len(rows) - 1} of the {case.B}-sequence workload ({len(rows) * case.Hkv} (sequence, "
+                      f"KV head) units on {used} threads), {reps} repetitions in {dt:.2f} s, block keys precomputed",
             "single_thread_value": round(reps1 / dt1, 3),
             "single_thread_sample": f"sequence 0 on 1 thread, {reps1} repetitions in {dt1:.2f} s",
-            "cpu_model": cpu_model()}
+            "host_threads": threads, "cpu_model": cpu_model()}
+
+
+def traffic_record(case):
+    """HBM bytes per launch of the scan from the committed PMC summary of this
+    workload, or None when the scan's sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"scores_stream_kernel_{case.name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if (rec.get("source_sha256_16") == source_hash(SCORES_SRC) and rec.get("workload") == case.name
+            and rec.get("ckey_dtype", "fp32") == case.ckey_dtype and rec.get("kv_dtype", "bf16") == case.kv_dtype):
+        return rec.get("hbm_bytes_per_launch")
+    return None
+
+
+class Timer:
+    """HIP events on the current stream (the one the library launches on)."""
+
+    def __init__(self, steps: int, marks: int):
+        import torch
+
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(steps)]
+
+    def ms(self):
+        import numpy as np
+
+        return np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(len(ev) - 1)] for ev in self.ev])
+
+
+def decode_record(name: str, args, headline: bool) -> dict:
+    """Measure one decode workload: the step, its kernels, its roofline and (unless
+    disabled) its CPU oracle baseline."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_compress_amd as qsa
+    import synth
+    from block_sparse_attention_compress_amd.pipeline import (DecodeBuffers, DecodeGraph, FusedDecodeBuffers,
+                                                             decode_step, decode_step_fused)
+
+    case = synth.config(name)
+    case.ckey_dtype = args.ckey
+    case.kv_dtype = args.kv
+    log(f"workload {case.name}: B={case.B} lens {int(case.lens.min())}..{int(case.lens.max())} "
+        f"heads ({case.Hq},{case.Hkv}) page {case.page_size}")
+    t0 = time.perf_counter()
+    dev = synth.to_device(case, "cuda")
+    case.drop_paged()
+    log(f"{name}: inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
+    q, q_pos = dev["q"], dev["q_pos"]
+    stride = (max(case.nb(i) for i in range(case.B)) + 63) // 64 * 64  # 16-byte rows for the selection's loads
+    buf = DecodeBuffers.allocate(case.B, case.Hq, case.Hkv, stride, case.topk, 0, "cuda")
+    steps, warmup = args.steps, args.warmup
+
+    # full block-key build (prefill-time work, timed on its own)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qsa.qsa_compress_keys(kv)
+    e0.record()
+    qsa.qsa_compress_keys(kv)
+    e1.record()
+    torch.cuda.synchronize()
+    compress_full_ms = e0.elapsed_time(e1)
+
+    internal = 0 if args.splits is None else args.splits
+    ws, tw = buf.workspace, buf.topk_workspace
+    S = case.splits                                            # > 1: the workload names interleaved partials
+    part_out = part_lse = None
+    if S > 1:
+        part_out = torch.empty((S, case.B, case.Hq, 256), dtype=torch.float32, device="cuda")
+        part_lse = torch.empty((S, case.B, case.Hq), dtype=torch.float32, device="cuda")
+    N = case.B * case.Hq
+
+    def scan():
+        qsa.qsa_decode_scores_refresh(kv, q, q.stride(0), case.Hq, buf.scores, stride)
+
+    def topk():
+        qsa.qsa_topk_blocks_ws(buf.scores, stride, q_pos, case.B, case.Hkv, case.topk, buf.sel_idx, buf.sel_cnt,
+                               workspace=tw, workspace_bytes=0 if tw is None else tw.numel())
+
+    def attn_internal():
+        qsa.qsa_sparse_attn_decode(kv, q, q.stride(0), case.Hq, buf.sel_idx, buf.sel_cnt, case.topk, case.scale,
+                                   internal, buf.out, buf.out.stride(0), buf.lse, workspace=ws,
+                                   workspace_bytes=0 if ws is None else ws.numel())
+
+    def attn_partials():
+        qsa.qsa_sparse_attn_decode(kv, q, q.stride(0), case.Hq, buf.sel_idx, buf.sel_cnt, case.topk, case.scale,
+                                   S, None, 0, None, part_out, part_lse)
+
+    def merge():
+        qsa.qsa_merge_lse(part_out, part_lse, S, N, 256, buf.out, buf.lse)
+
+    # the step as the workload names it: for C5 the interleaved partials and the merge
+    launches = [scan, topk] + ([attn_partials, merge] if S > 1 else [attn_internal])
+    names = ["refresh_and_scores", "topk"] + (["attention_partials", "merge_lse"] if S > 1 else
+                                              ["attention_and_merge"])
+
+    def step(ev=None):
+        for j, f in enumerate(launches):
+            if ev is not None:
+                ev[j].record()
+            f()
+        if ev is not None:
+            ev[len(launches)].record()
+
+    def wall(fn, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / n * 1e3
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # (1) eager steps with HIP events between the launches: per-kernel times
+    tm = Timer(steps, len(launches) + 1)
+    for i in range(steps):
+        step(tm.ev[i])
+    torch.cuda.synchronize()
+    part_ms = tm.ms().mean(axis=0)
+    # (2) eager steps, nothing between the launches
+    eager_ms = wall(step, steps)
+    ms_per_step, mode = eager_ms, "eager"
+    # (3) optionally, the step captured once in a HIP graph and replayed
+    if args.graph and S == 1:
+        graph = DecodeGraph(kv, q, q_pos, buf, scale=case.scale, num_splits=internal)
+        for _ in range(warmup):
+            graph.replay()
+        ms_per_step, mode = wall(graph.replay, steps), "hip-graph replay"
+
+    # the internal split beside the named interleaved path (C5)
+    internal_rec = None
+    if S > 1:
+        for _ in range(warmup):
+            decode_step(kv, q, q_pos, buf, scale=case.scale, num_splits=internal)
+        ims = wall(lambda: decode_step(kv, q, q_pos, buf, scale=case.scale, num_splits=internal), steps)
+        internal_rec = {"ms_per_step": round(ims, 4), "queries_per_s": round(case.B / (ims / 1e3), 1),
+                        "path": "qsa_decode_scores_refresh, qsa_topk_blocks_ws, qsa_sparse_attn_decode with the "
+                                "library's split count (contiguous block ranges, merged inside the call)"}
+
+    # (4) optionally, cold-cache steps: a 1 GiB read before each one evicts L2 and the MALL
+    cold = None
+    if args.flush:
+        junk = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        cold_ms = []
+        for i in range(steps):
+            junk.sum()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            step()
+            c1.record()
+            torch.cuda.synchronize()
+            cold_ms.append(c0.elapsed_time(c1))
+        del junk
+        cm = float(np.median(cold_ms))
+        cold = {"ms_per_step_median": round(cm, 4), "queries_per_s": round(case.B / (cm / 1e3), 1),
+                "flush_bytes_read": 1 << 30}
+
+    # (5) the fused single-launch step (qsa_decode_fused), reported beside the step
+    fused = None
+    if not args.no_fused:
+        fb = FusedDecodeBuffers.allocate(kv, case.Hq, case.topk, internal)
+        for _ in range(warmup):
+            decode_step_fused(kv, q, q_pos, fb, scale=case.scale)
+        fms = wall(lambda: decode_step_fused(kv, q, q_pos, fb, scale=case.scale), steps)
+        fused = {"ms_per_step": round(fms, 4), "queries_per_s": round(case.B / (fms / 1e3), 1),
+                 "vs_step": round(ms_per_step / fms, 3),
+                 "selection_equal": bool(torch.equal(fb.sel_idx, buf.sel_idx)),
+                 "abandoned_waits": int(fb.workspace[8:12].view(torch.int32).item())}
+        del fb
+
+    # the selection of the timed path (identical for every path: same scores, same select)
+    step()
+    torch.cuda.synchronize()
+    sel = buf.sel_idx.cpu().numpy()
+    cnt = buf.sel_cnt.cpu().numpy()
+    by = decode_bytes(case, sel, cnt, case.page_size, S)
+    scan_ms = float(part_ms[0])
+    achieved = by["scan"] / (scan_ms / 1e3) / 1e9
+    step_gbs = by["step"] / (ms_per_step / 1e3) / 1e9
+
+    rec = {
+        "workload": describe(case),
+        "batch": case.B, "mean_context": float(case.lens.mean()), "topk_blocks": case.topk,
+        "queries_per_s": round(case.B / (ms_per_step / 1e3), 1),
+        "ms_per_step": round(ms_per_step, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(case),
+                     "kernel": "scores_stream_kernel (newest block key rebuilt + block-score scan)",
+                     "algorithmic_bytes_per_launch": by["scan"],
+                     "overhead_bytes_per_launch": by["scan_overhead"],
+                     "avg_launch_ms": round(scan_ms, 5),
+                     "step_algorithmic_bytes": by["step"],
+                     "step_achieved": round(step_gbs, 1),
+                     "step_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "step": {"path": " -> ".join(names), "selected_tokens": by["tokens"],
+                 "overhead_bytes": by["step_overhead"],
+                 "event_ms": {n: round(float(m), 5) for n, m in zip(names, part_ms)},
+                 "execution": mode, "eager_ms_per_step": round(eager_ms, 4),
+                 "internal_split": internal_rec, "fused_single_launch": fused, "cold_cache": cold,
+                 "full_block_key_build_ms": round(compress_full_ms, 4)},
+    }
+    del dev, kv, q, q_pos, buf, part_out, part_lse
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        secs = args.cpu_seconds if headline else 0.4 * args.cpu_seconds
+        rows = {"C1": 1, "C2": 8, "C3": 4, "C5": 16}[name]
+        t0 = time.perf_counter()
+        rec["cpu_baseline"] = cpu_baseline(case, secs, rows)
+        log(f"{name}: cpu baseline in {time.perf_counter() - t0:.1f} s")
+    return rec
 
 
 def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv_dtype: str = "bf16"):
     """Extend chunk: 4096 new query tokens on 28672 cached (32768 total), (12, 1) heads."""
+    import numpy as np
     import torch
 
     import block_sparse_attention_compress_amd as qsa
@@ -205,223 +451,111 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
     qsa.qsa_compress_keys(kv)                                  # cached blocks
     stride = case.nb(0)
     buf = ExtendBuffers.allocate(case.R, case.Hq, case.Hkv, stride, 512, "cuda")
+    q, q_seq, q_pos = dev["q"], dev["q_seq"], dev["q_pos"]
+    R, Hq, Hkv = case.R, case.Hq, case.Hkv
+    launches = [
+        lambda: qsa.qsa_compress_keys(kv, first, 0),
+        lambda: qsa.qsa_block_scores(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.scores, stride),
+        lambda: qsa.qsa_topk_blocks(buf.scores, stride, q_pos, R, Hkv, 512, buf.sel_idx, buf.sel_cnt),
+        lambda: qsa.qsa_sparse_attn_extend(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.sel_idx, buf.sel_cnt, 512,
+                                           case.scale, buf.out, buf.out.stride(0), buf.lse),
+    ]
+    names = ["block_keys", "scores", "topk", "attention"]
     for _ in range(2):
-        extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, first, case.R, scale=case.scale)
+        extend_step(kv, q, q_seq, q_pos, buf, first, scale=case.scale)
     torch.cuda.synchronize()
+    tm = Timer(steps, len(launches) + 1)
+    for i in range(steps):
+        for j, f in enumerate(launches):
+            tm.ev[i][j].record()
+            f()
+        tm.ev[i][len(launches)].record()
+    torch.cuda.synchronize()
+    part_ms = tm.ms().mean(axis=0)
     t0 = time.perf_counter()
     for _ in range(steps):
-        extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, first, case.R, scale=case.scale)
+        extend_step(kv, q, q_seq, q_pos, buf, first, scale=case.scale)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
     cold = None
     if flush:  # a 1 GiB read before each chunk evicts L2 and the MALL
-        import numpy as np
         junk = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         ms = []
         for i in range(steps):
             junk.sum()
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             c0.record()
-            extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, first, case.R, scale=case.scale)
+            extend_step(kv, q, q_seq, q_pos, buf, first, scale=case.scale)
             c1.record()
             torch.cuda.synchronize()
             ms.append(c0.elapsed_time(c1))
         del junk
         cold = round(float(np.median(ms)), 4)
-    # MFMA work: scores 2*256 per eligible block per row; attention 2 * 2 * 256 per
-    # (selected token, real head)
+    # matrix-core work: scores 2*256 per eligible block per row; attention 2 * 2 * 256
+    # per (selected token, real head)
     elig = sum(min(int(t) // 4 + 1, stride) for t in case.q_pos)
     cnt = buf.sel_cnt.cpu().numpy()
-    flops = 2 * 256 * elig + 4 * 256 * case.Hq * int(cnt.sum()) * 4
+    score_flops = 2 * 256 * elig
+    attn_flops = 4 * 256 * case.Hq * int(cnt.sum()) * 4
     return {"workload": f"extend: 4096 new tokens on 28672 cached, (12,1) heads, top-512 per query, "
                         f"{kv_dtype} K/V, {ckey_dtype} block keys",
             "new_tokens_per_s": round(case.R / dt, 1), "ms_per_chunk": round(dt * 1e3, 4),
-            "tflops": round(flops / dt / 1e12, 2), "cold_cache_ms_per_chunk_median": cold}
+            "tflops": round((score_flops + attn_flops) / dt / 1e12, 2),
+            "event_ms": {n: round(float(m), 5) for n, m in zip(names, part_ms)},
+            "scores_tflops": round(score_flops / (part_ms[1] / 1e3) / 1e12, 2),
+            "scores_frac_of_fp32_matrix_peak": round(score_flops / (part_ms[1] / 1e3) / 157.3e12, 4),
+            "attention_tflops": round(attn_flops / (part_ms[3] / 1e3) / 1e12, 2),
+            "cold_cache_ms_per_chunk_median": cold}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+              f"run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     if args.copy_calibration:
         copy_calibration()
         return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.extend_only:
-        assert torch.cuda.is_available(), "bench.py needs a GPU"
         print(json.dumps(extend_figures(args.steps, args.flush, args.ckey, args.kv)), flush=True)
         return
     import block_sparse_attention_compress_amd as qsa
-    import synth
-    from block_sparse_attention_compress_amd.pipeline import (DecodeBuffers, DecodeGraph, FusedDecodeBuffers,
-                                                             decode_step, decode_step_fused)
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     qsa.lib()
-    case = synth.config(args.config)
-    case.ckey_dtype = args.ckey
-    case.kv_dtype = args.kv
-    log(f"workload {case.name}: B={case.B} lens {int(case.lens.min())}..{int(case.lens.max())} "
-        f"heads ({case.Hq},{case.Hkv}) page {case.page_size}")
-    t0 = time.perf_counter()
-    dev = synth.to_device(case, "cuda")
-    case.drop_paged()
-    log(f"inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
-    kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
-    q, q_pos = dev["q"], dev["q_pos"]
-    stride = (max(case.nb(i) for i in range(case.B)) + 63) // 64 * 64  # 16-byte rows for the selection's loads
-    buf = DecodeBuffers.allocate(case.B, case.Hq, case.Hkv, stride, case.topk, 0, "cuda")
-
-    # full block-key build (prefill-time work, timed on its own)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    qsa.qsa_compress_keys(kv)
-    e0.record()
-    qsa.qsa_compress_keys(kv)
-    e1.record()
-    torch.cuda.synchronize()
-    compress_full_ms = e0.elapsed_time(e1)
-
-    splits = (0 if case.splits == 1 else case.splits) if args.splits is None else args.splits
-    ws, tw = buf.workspace, buf.topk_workspace
-
-    def step(ev=None):
-        # the same calls as pipeline.decode_step, with events between the launches
-        if ev is not None:
-            ev[0].record()
-        qsa.qsa_decode_scores_refresh(kv, q, q.stride(0), case.Hq, buf.scores, stride)
-        if ev is not None:
-            ev[1].record()
-        qsa.qsa_topk_blocks_ws(buf.scores, stride, q_pos, case.B, case.Hkv, case.topk, buf.sel_idx, buf.sel_cnt,
-                               workspace=tw, workspace_bytes=0 if tw is None else tw.numel())
-        if ev is not None:
-            ev[2].record()
-        qsa.qsa_sparse_attn_decode(kv, q, q.stride(0), case.Hq, buf.sel_idx, buf.sel_cnt, case.topk, case.scale,
-                                   splits, buf.out, buf.out.stride(0), buf.lse, workspace=ws,
-                                   workspace_bytes=0 if ws is None else ws.numel())
-        if ev is not None:
-            ev[3].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # (1) eager steps with HIP events between the launches: per-kernel times
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    parts = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(3)] for ev in events])  # ms
-    part_ms = parts.mean(axis=0)
-    # (2) eager steps, nothing between the launches
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        decode_step(kv, q, q_pos, buf, scale=case.scale, num_splits=splits)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t1) / args.steps * 1e3
-    # (3) optionally, the same step captured once in a HIP graph and replayed (on
-    # this stack the eager launches already run back to back, so eager is faster)
-    ms_per_step = eager_ms
-    mode = "eager"
-    if args.graph:
-        graph = DecodeGraph(kv, q, q_pos, buf, scale=case.scale, num_splits=splits)
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
-        mode = "hip-graph replay"
-
-    # (3b) optionally, cold-cache steps: a 1 GiB read before each one evicts L2 and
-    # the 256 MB MALL (a read, so no dirty lines are left to write back during the
-    # step); HIP events bracket the step alone (median reported)
-    cold = None
-    if args.flush:
-        junk = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        cold_ms = []
-        for i in range(args.steps):
-            junk.sum()
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record()
-            decode_step(kv, q, q_pos, buf, scale=case.scale, num_splits=splits)
-            c1.record()
-            torch.cuda.synchronize()
-            cold_ms.append(c0.elapsed_time(c1))
-        del junk
-        cm = float(np.median(cold_ms))
-        cold = {"ms_per_step_median": round(cm, 4), "queries_per_s": round(case.B / (cm / 1e3), 1),
-                "flush_bytes_read": 1 << 30}
-
-    # (4) the fused single-launch step (qsa_decode_fused), reported beside the
-    # headline; its selection must equal the separate calls'
-    fused = None
-    if not args.no_fused:
-        fb = FusedDecodeBuffers.allocate(kv, case.Hq, case.topk, splits)
-        for _ in range(args.warmup):
-            decode_step_fused(kv, q, q_pos, fb, scale=case.scale)
-        torch.cuda.synchronize()
-        t2 = time.perf_counter()
-        for _ in range(args.steps):
-            decode_step_fused(kv, q, q_pos, fb, scale=case.scale)
-        torch.cuda.synchronize()
-        fused_ms = (time.perf_counter() - t2) / args.steps * 1e3
-        fused = {"ms_per_step": round(fused_ms, 4), "queries_per_s": round(case.B / (fused_ms / 1e3), 1),
-                 "selection_equal": bool(torch.equal(fb.sel_idx, buf.sel_idx)),
-                 "abandoned_waits": int(fb.workspace[8:12].view(torch.int32).item())}
-        del fb
-
-    sel = buf.sel_idx.cpu().numpy()
-    cnt = buf.sel_cnt.cpu().numpy()
-    step_bytes, scores_bytes, tokens = decode_bytes(case, sel, cnt, case.page_size)
-    scores_s = part_ms[0] / 1e3
-    achieved = scores_bytes / scores_s / 1e9
-
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
-        if (rec.get("source_sha256_16") == source_hash(SCORES_SRC) and rec.get("workload") == case.name
-                and rec.get("ckey_dtype", "fp32") == case.ckey_dtype and rec.get("kv_dtype", "bf16") == case.kv_dtype):
-            traffic = rec.get("hbm_bytes_per_launch")
-
+    names = DECODE_CONFIGS if args.config == "all" else (args.config,)
+    records = {}
+    for i, name in enumerate(names):
+        records[name] = decode_record(name, args, headline=(i == 0))
+    head_name = names[0]
+    head = records[head_name]
     result = {
         "metric": METRIC,
-        "value": round(case.B / (ms_per_step / 1e3), 1),
+        "value": head["queries_per_s"],
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": DTYPE if (args.ckey, args.kv) == ("fp32", "bf16") else f"{args.ckey} block keys, {args.kv} K/V",
         "data": "synthetic (seeded SplitMix64/Box-Muller bf16 K/V and queries)",
-        "config": {"workload": describe(case),
-                   "batch": case.B, "mean_context": float(case.lens.mean()), "topk_blocks": case.topk,
-                   "parallelism": "1 GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "scores_stream_kernel (newest block key rebuilt + block-score scan)",
-                     "algorithmic_bytes_per_launch": scores_bytes, "avg_launch_ms": round(part_ms[0], 5)},
-        "step": {"algorithmic_bytes": step_bytes, "algorithmic_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
-                 "selected_tokens": tokens,
-                 "event_ms": {"refresh_and_scores": round(part_ms[0], 5), "topk": round(part_ms[1], 5),
-                              "attention_and_merge": round(part_ms[2], 5)},
-                 "execution": mode, "eager_ms_per_step": round(eager_ms, 4), "fused_single_launch": fused,
-                 "cold_cache": cold,
-                 "full_block_key_build_ms": round(compress_full_ms, 4)},
+        "config": {"workload": head["workload"], "batch": head["batch"], "mean_context": head["mean_context"],
+                   "topk_blocks": head["topk_blocks"], "parallelism": "1 GPU"},
+        "roofline": head["roofline"],
+        "step": head["step"],
     }
+    if "cpu_baseline" in head:
+        result["cpu_baseline"] = head["cpu_baseline"]
+    if len(names) > 1:
+        result["configs"] = {n: records[n] for n in names[1:]}
     if not args.no_extend:
         result["extend"] = extend_figures(max(3, args.steps // 4), args.flush, args.ckey, args.kv)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

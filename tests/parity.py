@@ -23,6 +23,17 @@ def check_close(gpu, ref, what: str):
                              f"gpu {gpu[i]} oracle {ref[i]}")
 
 
+def tol_ratio(gpu, ref) -> float:
+    """The largest |gpu - oracle| / (ATOL + RTOL |oracle|) over the finite entries:
+    the share of the output tolerance that the GPU result uses (1 = at the bound)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(ref)
+    if not np.any(fin):
+        return 0.0
+    return float(np.max(np.abs(gpu[fin] - ref[fin]) / (ATOL + RTOL * np.abs(ref[fin]))))
+
+
 def check_lse(gpu, ref, what: str):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
