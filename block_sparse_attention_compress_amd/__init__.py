@@ -8,7 +8,8 @@ are in ``include/qsa.h``.  The functions keep the C names:
 
     qsa_compress_keys, qsa_block_scores, qsa_decode_scores_refresh, qsa_topk_blocks, qsa_topk_blocks_ws,
     qsa_sparse_attn_decode, qsa_sparse_attn_extend, qsa_merge_lse,
-    qsa_decode_fused (scores + top-k + attention + merge in one launch)
+    qsa_decode_fused (scores + top-k + attention + merge in one launch),
+    qsa_sparse_attn_decode_noalloc (decode attention with no workspace: static device scratch)
 
 Importing this module does not need a GPU; calling a function that launches
 work does.  If ``libqsa.so`` has not been built, loading fails with an error:
@@ -42,7 +43,7 @@ KV_FP8 = 1
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_compress_keys", "qsa_block_scores", "qsa_topk_blocks",
            "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse",
            "qsa_decode_fused", "qsa_decode_fused_workspace_bytes", "qsa_topk_blocks_ws",
-           "qsa_topk_workspace_bytes", "qsa_decode_scores_refresh")
+           "qsa_topk_workspace_bytes", "qsa_decode_scores_refresh", "qsa_sparse_attn_decode_noalloc")
 
 
 class QsaError(RuntimeError):
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_topk_workspace_bytes.argtypes, L.qsa_topk_workspace_bytes.restype = [i32, i32, i32, i32], sz
         L.qsa_sparse_attn_decode.argtypes = [kvp, vp, i64, i32, vp, vp, i32, f32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
         L.qsa_decode_workspace_bytes.argtypes, L.qsa_decode_workspace_bytes.restype = [i32, i32, i32], sz
+        L.qsa_sparse_attn_decode_noalloc.argtypes = [kvp, vp, i64, i32, vp, vp, i32, f32, i32, vp, i64, vp, vp]
         L.qsa_sparse_attn_extend.argtypes = [kvp, vp, i64, vp, vp, i32, i32, vp, vp, i32, f32, vp, i64, vp, vp]
         L.qsa_merge_lse.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.qsa_decode_fused.argtypes = [kvp, vp, i64, i32, i32, f32, i32, vp, vp, vp, i64, vp, vp, sz, vp]
@@ -210,6 +212,14 @@ def qsa_sparse_attn_decode(kv, q, q_row_stride: int, Hq: int, sel_idx, sel_cnt, 
     _check(lib().qsa_sparse_attn_decode(ctypes.byref(d), _ptr(q), q_row_stride, Hq, _ptr(sel_idx), _ptr(sel_cnt), k,
                                         scale, num_splits, _ptr(out), out_row_stride, _ptr(lse), _ptr(part_out),
                                         _ptr(part_lse), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qsa_sparse_attn_decode_noalloc(kv, q, q_row_stride: int, Hq: int, sel_idx, sel_cnt, k: int, scale: float,
+                                   num_splits: int, out, out_row_stride: int, lse=None, stream=None) -> None:
+    d = _kv(kv)
+    _check(lib().qsa_sparse_attn_decode_noalloc(ctypes.byref(d), _ptr(q), q_row_stride, Hq, _ptr(sel_idx),
+                                                _ptr(sel_cnt), k, scale, num_splits, _ptr(out), out_row_stride,
+                                                _ptr(lse), _stream(stream)))
 
 
 def qsa_sparse_attn_extend(kv, q, q_row_stride: int, q_seq, q_pos, R: int, Hq: int, sel_idx, sel_cnt, k: int,

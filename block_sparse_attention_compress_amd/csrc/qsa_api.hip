@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "qsa.h"
 #include "qsa_launch.h"
 
@@ -116,6 +118,78 @@ int auto_splits(int64_t units, int k) {
 }
 
 constexpr int kAutoSplitMax = 16;
+
+// ---- static scratch of the no-allocation decode entry point
+//
+// The split partials of qsa_sparse_attn_decode_noalloc live in this array: one
+// copy per GPU, loaded with the code object and held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it names a
+// host-side stand-in): the device address is looked up once per device, with
+// that device current, and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = QSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(QSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return QSA_OK;
+}
+
+// Decode attention writing the final result (out, lse): one launch when the split
+// count is 1, else blocked split partials and the merge.  The partials go to the
+// caller's `workspace`, or with use_scratch to the static scratch (the
+// no-allocation entry point; workspace is then ignored).
+int decode_final(const qsa::PagedKV& p, const qsa::Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt,
+                 int32_t k, float sc, int32_t num_splits, void* out, int64_t out_row_stride, float* lse,
+                 void* workspace, size_t workspace_bytes, bool use_scratch, hipStream_t st, const char* what) {
+    const int Hq = rows.Hq;
+    if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
+    if (out_row_stride < (int64_t)Hq * QSA_HEAD_DIM)
+        return fail(QSA_ERR_INVALID_ARG, "out_row_stride %lld < Hq * 256", (long long)out_row_stride);
+    const int S = num_splits == 0 ? auto_splits((int64_t)p.batch * p.Hkv, k) : num_splits;
+    if (S == 1) {
+        qsa::AttnOut o{static_cast<uint16_t*>(out), out_row_stride, lse, nullptr, nullptr};
+        return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, false, o, st), what);
+    }
+    if (out_row_stride != (int64_t)Hq * QSA_HEAD_DIM || !aligned(out, 8))
+        return fail(QSA_ERR_UNSUPPORTED, "a split decode writes a dense, 8-byte aligned out");
+    const size_t need = qsa_decode_workspace_bytes(p.batch, Hq, S);
+    if (use_scratch) {
+        if (need > kScratchBytes)
+            return fail(QSA_ERR_UNSUPPORTED,
+                        "%d splits of %d rows x %d heads need %zu bytes of partials, more than the %zu bytes of "
+                        "static scratch (use qsa_sparse_attn_decode with a workspace, or fewer splits)",
+                        S, p.batch, Hq, need, (size_t)kScratchBytes);
+        if (int rc = scratch_for_current_device(&workspace)) return rc;
+        workspace_bytes = kScratchBytes;
+    } else if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) {
+        return fail(QSA_ERR_INVALID_ARG, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    }
+    const int64_t n = (int64_t)S * p.batch * Hq;
+    float* wo = static_cast<float*>(workspace);
+    float* wl = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         (((size_t)n * QSA_HEAD_DIM * sizeof(float) + 255) & ~(size_t)255));
+    qsa::AttnOut o{nullptr, 0, nullptr, wo, wl};
+    if (int rc = hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, S, true, o, st), what)) return rc;
+    return hip_status(qsa::launch_merge(wo, wl, S, p.batch * Hq, QSA_HEAD_DIM, static_cast<uint16_t*>(out), lse, st),
+                      what);
+}
+
 
 }  // namespace
 
@@ -252,29 +326,27 @@ int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
         return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, num_splits, false, o, st),
                           "qsa_sparse_attn_decode");
     }
-    if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
-    if (out_row_stride < (int64_t)Hq * QSA_HEAD_DIM)
-        return fail(QSA_ERR_INVALID_ARG, "out_row_stride %lld < Hq * 256", (long long)out_row_stride);
-    const int S = num_splits == 0 ? auto_splits((int64_t)p.batch * p.Hkv, k) : num_splits;
-    if (S == 1) {
-        qsa::AttnOut o{static_cast<uint16_t*>(out), out_row_stride, lse, nullptr, nullptr};
-        return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, false, o, st), "qsa_sparse_attn_decode");
-    }
-    if (out_row_stride != (int64_t)Hq * QSA_HEAD_DIM || !aligned(out, 8))
-        return fail(QSA_ERR_UNSUPPORTED, "a split decode writes a dense, 8-byte aligned out");
-    const size_t need = qsa_decode_workspace_bytes(p.batch, Hq, S);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-        return fail(QSA_ERR_INVALID_ARG, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-                    workspace_bytes);
-    const int64_t n = (int64_t)S * p.batch * Hq;
-    float* wo = static_cast<float*>(workspace);
-    float* wl = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         (((size_t)n * QSA_HEAD_DIM * sizeof(float) + 255) & ~(size_t)255));
-    qsa::AttnOut o{nullptr, 0, nullptr, wo, wl};
-    if (int rc = hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, S, true, o, st), "qsa_sparse_attn_decode"))
-        return rc;
-    return hip_status(qsa::launch_merge(wo, wl, S, p.batch * Hq, QSA_HEAD_DIM, static_cast<uint16_t*>(out), lse, st),
-                      "qsa_sparse_attn_decode (merge)");
+    return decode_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, workspace,
+                        workspace_bytes, false, st, "qsa_sparse_attn_decode");
+}
+
+int qsa_sparse_attn_decode_noalloc(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq,
+                                   const int32_t* sel_idx, const int32_t* sel_cnt, int32_t k, float scale,
+                                   int32_t num_splits, void* out, int64_t out_row_stride, float* lse, void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, true, true, false, &p)) return rc;
+    if (int rc = check_heads(Hq, p.Hkv)) return rc;
+    if (int rc = check_q(q, q_row_stride, Hq)) return rc;
+    if (k < 0 || k > QSA_MAX_TOPK) return fail(QSA_ERR_INVALID_ARG, "k %d out of [0, %d]", k, QSA_MAX_TOPK);
+    if (!sel_cnt || (k > 0 && !sel_idx)) return fail(QSA_ERR_INVALID_ARG, "sel_idx / sel_cnt is NULL");
+    if (num_splits < 0 || num_splits > QSA_MAX_SPLITS)
+        return fail(QSA_ERR_INVALID_ARG, "num_splits %d out of [0, %d]", num_splits, QSA_MAX_SPLITS);
+    if ((int64_t)p.batch * p.Hkv * (num_splits > 0 ? num_splits : kAutoSplitMax) > 0x7fffffff)
+        return fail(QSA_ERR_UNSUPPORTED, "too many work units");
+    const float sc = scale > 0.f ? scale : 0.0625f;
+    qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, nullptr, nullptr, p.batch, Hq};
+    return decode_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, nullptr, 0, true,
+                        static_cast<hipStream_t>(stream), "qsa_sparse_attn_decode_noalloc");
 }
 
 size_t qsa_decode_fused_workspace_bytes(const qsa_kv_t* kv, int32_t Hq, int32_t k, int32_t num_splits) {

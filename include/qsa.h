@@ -63,6 +63,7 @@ extern "C" {
 #define QSA_CKEY_FP8 2              /* block keys stored as fp8 E4M3 (rounded, saturated fp32 means) */
 #define QSA_KV_BF16 0               /* K and V rows stored as bf16 */
 #define QSA_KV_FP8 1                /* K and V rows stored as fp8 E4M3 codes, unit scale */
+#define QSA_NOALLOC_SCRATCH_BYTES (8u << 20) /* static device scratch of qsa_sparse_attn_decode_noalloc, per GPU */
 
 /*
  * Paged KV cache.  Page p of the pool holds, for every KV head, page_size
@@ -241,6 +242,30 @@ QSA_API int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_
 /* Workspace bytes qsa_sparse_attn_decode needs for num_splits (0 = the
  * library's own choice) when it writes the final result. */
 QSA_API size_t qsa_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t num_splits);
+
+/*
+ * qsa_sparse_attn_decode without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture that must not call hipMalloc, tight serving loops that keep a fixed
+ * memory budget, and harnesses that forbid allocation.  The same computation and result, bit for bit,
+ * as qsa_sparse_attn_decode writing the final result (part_out == NULL) with the same num_splits
+ * (0 = the library's choice); the arguments mean the same.
+ *
+ * The split partials (qsa_decode_workspace_bytes(batch, Hq, S) bytes for the split count S used) live
+ * in a static device array of QSA_NOALLOC_SCRATCH_BYTES (8 MiB), one per GPU, held from the library's
+ * load until the process ends.  The library looks its address up once per device, on the first call
+ * with that device current.  The call allocates nothing and calls no allocating routine.  Nothing in the
+ * scratch needs clearing: every partial the merge reads is written earlier in the same call.
+ *
+ * Errors: as qsa_sparse_attn_decode; QSA_ERR_UNSUPPORTED, with a message and nothing launched, when the
+ * partials would exceed QSA_NOALLOC_SCRATCH_BYTES (use qsa_sparse_attn_decode with a workspace, or fewer
+ * splits); QSA_ERR_HIP if the scratch's address cannot be looked up.  All calls on one GPU share its
+ * scratch: calls that may overlap on one GPU (several streams, several host threads) race and must be
+ * ordered by the caller, e.g. issued on one stream.
+ */
+QSA_API int qsa_sparse_attn_decode_noalloc(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq,
+                                           const int32_t* sel_idx, const int32_t* sel_cnt, int32_t k, float scale,
+                                           int32_t num_splits, void* out, int64_t out_row_stride, float* lse,
+                                           void* stream);
 
 /*
  * Fused decode (source as for a2-a5: "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat

@@ -281,3 +281,15 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(qsa, "LIB_PATH", str(tmp_path / "libqsa.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         qsa.lib()
+
+
+def test_noalloc_decode_rejects_partials_beyond_the_scratch_on_the_host():
+    """qsa_sparse_attn_decode_noalloc: partials beyond QSA_NOALLOC_SCRATCH_BYTES are
+    rejected before any HIP call (64 splits x 1000 rows x 16 heads)."""
+    d = kv(batch=1000)
+    rc = status("qsa_sparse_attn_decode_noalloc", ctypes.byref(d), P, 16 * 256, 16, P, P, 512, ctypes.c_float(0.0),
+                64, P, 16 * 256, P, None)
+    assert rc == qsa.QSA_ERR_UNSUPPORTED
+    assert "scratch" in qsa.qsa_last_error()
+    text = open(HEADER).read()
+    assert re.search(r"#define QSA_NOALLOC_SCRATCH_BYTES \(8u << 20\)", text)
