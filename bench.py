@@ -78,7 +78,10 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--graph", action="store_true", help="time a replayed HIP graph of the step instead of eager launches")
     p.add_argument("--splits", type=int, default=None, help="decode split count (default: the library's choice)")
-    p.add_argument("--no-fused", action="store_true", help="skip the single-launch fused step figures")
+    p.add_argument("--no-fused", action="store_true", help="do not time the fused step (the default)")
+    p.add_argument("--fused", action="store_true",
+                   help="also time the single-launch fused step (qsa_decode_fused); slower than the separate calls "
+                        "on every workload measured, so not part of the default run")
     p.add_argument("--flush", action="store_true",
                    help="also time single steps after a 1 GiB read that evicts the caches (MALL included)")
     p.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
@@ -379,9 +382,9 @@ def decode_record(name: str, args, headline: bool) -> dict:
         cold = {"ms_per_step_median": round(cm, 4), "queries_per_s": round(case.B / (cm / 1e3), 1),
                 "flush_bytes_read": 1 << 30}
 
-    # (5) the fused single-launch step (qsa_decode_fused), reported beside the step
+    # (5) optionally, the fused single-launch step (qsa_decode_fused), beside the step
     fused = None
-    if not args.no_fused:
+    if args.fused:
         fb = FusedDecodeBuffers.allocate(kv, case.Hq, case.topk, internal)
         for _ in range(warmup):
             decode_step_fused(kv, q, q_pos, fb, scale=case.scale)

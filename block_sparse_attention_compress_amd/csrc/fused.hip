@@ -433,38 +433,60 @@ __device__ __forceinline__ void select_unit(const float* __restrict__ s, int n, 
 
 // out / lse of the g heads of (row, KV head h) from the S partials (natural-log
 // lse; all -inf gives 0 and -inf; a NaN partial, left by an abandoned wait, makes
-// the result NaN), 4 dims per thread.
-__device__ __forceinline__ void merge_unit(const FusedParams& F, int row, int h) {
+// the result NaN).  lds: at least S * g + g floats.  The S x g partial lse are
+// read in one round (one per thread), the weights are formed in LDS, and every
+// thread then accumulates 4 dims of one head with up to 16 partial loads in
+// flight, so a merge costs about two memory round trips whatever S is.
+__device__ __forceinline__ void merge_unit(const FusedParams& F, int row, int h, float* lds) {
     const AttnParams& A = F.A;
     const int g = A.g, S = A.S;
-    for (int e = threadIdx.x; e < g * 64; e += kFusedThreads) {
-        const int head = h * g + (e >> 6);
-        const int d = 4 * (e & 63);
+    float* w = lds;           // [S][g] partial lse, then weights
+    float* hlse = lds + S * g;  // [g] merged lse
+    for (int e = threadIdx.x; e < S * g; e += kFusedThreads)
+        w[e] = A.part_lse[((int64_t)(e / g) * A.R + row) * A.Hq + h * g + e % g];
+    __syncthreads();
+    if (threadIdx.x < g) {
+        const int hh = threadIdx.x;
         float M = -INFINITY;
         for (int sp = 0; sp < S; ++sp) {
-            const float x = A.part_lse[((int64_t)sp * A.R + row) * A.Hq + head];
+            const float x = w[sp * g + hh];
             M = (x != x || M != M) ? __builtin_nanf("") : fmaxf(M, x);
         }
-        uint16_t* o = F.out + (int64_t)row * F.out_stride + (int64_t)head * kHeadDim + d;
-        if (M == -INFINITY) {
-            *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
-            if (d == 0 && F.lse) F.lse[(int64_t)row * A.Hq + head] = -INFINITY;
-            continue;
-        }
         float z = 0.f;
-        for (int sp = 0; sp < S; ++sp) z += expf(A.part_lse[((int64_t)sp * A.R + row) * A.Hq + head] - M);
+        if (M != -INFINITY)
+            for (int sp = 0; sp < S; ++sp) z += expf(w[sp * g + hh] - M);  // NaN M: z NaN
+        for (int sp = 0; sp < S; ++sp)
+            w[sp * g + hh] = M == -INFINITY ? 0.f : expf(w[sp * g + hh] - M) / z;
+        hlse[hh] = M == -INFINITY ? -INFINITY : M + logf(z);
+    }
+    __syncthreads();
+    constexpr int kBatch = 16;
+    for (int e = threadIdx.x; e < g * 64; e += kFusedThreads) {
+        const int hh = e >> 6;
+        const int head = h * g + hh;
+        const int d = 4 * (e & 63);
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp = 0; sp < S; ++sp) {
-            const int64_t pr = ((int64_t)sp * A.R + row) * A.Hq + head;
-            const float w = expf(A.part_lse[pr] - M) / z;
-            const float4 x = *reinterpret_cast<const float4*>(A.part_out + pr * kHeadDim + d);
-            acc.x += w * x.x;
-            acc.y += w * x.y;
-            acc.z += w * x.z;
-            acc.w += w * x.w;
+        for (int sp0 = 0; sp0 < S; sp0 += kBatch) {
+            float4 x[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                x[j] = sp0 + j < S ? *reinterpret_cast<const float4*>(
+                                         A.part_out + (((int64_t)(sp0 + j) * A.R + row) * A.Hq + head) * kHeadDim + d)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (sp0 + j >= S) break;
+                const float ws = w[(sp0 + j) * g + hh];
+                acc.x += ws * x[j].x;
+                acc.y += ws * x[j].y;
+                acc.z += ws * x[j].z;
+                acc.w += ws * x[j].w;
+            }
         }
+        if (hlse[hh] == -INFINITY) acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        uint16_t* o = F.out + (int64_t)row * F.out_stride + (int64_t)head * kHeadDim + d;
         *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
-        if (d == 0 && F.lse) F.lse[(int64_t)row * A.Hq + head] = M + logf(z);
+        if (d == 0 && F.lse) F.lse[(int64_t)row * A.Hq + head] = hlse[hh];
     }
 }
 
@@ -475,6 +497,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
     const FusedParams F) {
     extern __shared__ float smem[];
     __shared__ int sh_item, sh_last;
+    __shared__ float4 stash[4 * 64];  // each wave's rebuilt newest block key until it is scored
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = wave_id();
@@ -506,10 +529,27 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
             const int nch = max(1, (n_elig + kStreamChunk - 1) / kStreamChunk);
             if (j >= nch) continue;  // past the row: not counted
             const int wb0 = j * kStreamChunk + wave * (kStreamChunk / 4);
+            // the block holding the newest token (t = L - 1) is rebuilt from K and
+            // stored by the wave that scores it, or by the row's first wave when
+            // the score stride cuts the row short (as scores_stream_kernel does)
+            Refresh rf;
+            {
+                const int b = (L - 1) >> 2;
+                const bool scored = b < n_elig;
+                if (L > 0 && (scored ? (wb0 <= b && b < wb0 + kStreamChunk / 4) : wb0 == 0)) {
+                    rf.k = F.A.k;
+                    rf.kv8 = KV8;
+                    rf.ckey = const_cast<void*>(F.ckey);
+                    rf.b = b;
+                    rf.n = L - 4 * b;
+                    rf.score = scored;
+                    rf.stash = stash + wave * 64;
+                }
+            }
             if (wb0 < n_elig)
-                scan_wave<PAGE16, true, KT>(F.q + (int64_t)row * F.q_stride + (int64_t)h * F.g * kHeadDim, F.g,
-                                        F.ckey, F.block_table + (int64_t)row * F.max_pages, F.Hkv, h, F.lg_ps,
-                                        n_elig, wb0, lane, srow);
+                scan_wave<PAGE16, true, KT, true>(F.q + (int64_t)row * F.q_stride + (int64_t)h * F.g * kHeadDim,
+                                                  F.g, F.ckey, F.block_table + (int64_t)row * F.max_pages, F.Hkv, h,
+                                                  F.lg_ps, n_elig, wb0, lane, srow, rf);
             // The scores went out as device-scope stores: once every wave has seen
             // its own stores complete (the wait) and the barrier has passed, they are
             // visible device-wide, so the arrival needs no release (a release would
@@ -569,7 +609,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
             __syncthreads();
             if (!sh_last) continue;
             if (tid == 0) uc[2] = 0;
-            merge_unit(F, row, h);
+            merge_unit(F, row, h, smem);
         }
     }
     // the last workgroup out returns the ticket counters to zero and advances the

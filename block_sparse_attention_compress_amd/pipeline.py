@@ -69,7 +69,7 @@ def decode_step(kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: DecodeBu
 @dataclass
 class FusedDecodeBuffers:
     """Outputs and workspace of the fused decode step.  The workspace is zeroed
-    once here; the library leaves its control area zero after every call."""
+    once here; the library keeps its control area consistent from then on."""
 
     sel_idx: torch.Tensor     # int32 [B][Hkv][k]
     sel_cnt: torch.Tensor     # int32 [B][Hkv]
@@ -94,12 +94,10 @@ class FusedDecodeBuffers:
 
 
 def decode_step_fused(kv: KVCache, q: torch.Tensor, q_pos: torch.Tensor, buf: FusedDecodeBuffers, scale: float = 0.0,
-                      refresh_keys: bool = True, stream=None) -> None:
-    """The decode step in two launches: the block-key refresh of the newest token,
-    then scores, selection, attention and merge fused."""
+                      stream=None) -> None:
+    """The decode step in one launch: the newest token's block key rebuilt, then
+    scores, selection, attention and merge (q_pos is implied: L - 1)."""
     Hq = q.shape[1]
-    if refresh_keys:
-        qsa_compress_keys(kv, q_pos, 1, stream=stream)
     qsa_decode_fused(kv, q, q.stride(0), Hq, buf.k, scale, buf.num_splits, buf.sel_idx, buf.sel_cnt, buf.out,
                      buf.out.stride(0), buf.lse, workspace=buf.workspace, workspace_bytes=buf.workspace.numel(),
                      stream=stream)

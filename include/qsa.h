@@ -272,8 +272,10 @@ QSA_API int qsa_sparse_attn_decode_noalloc(const qsa_kv_t* kv, const void* q, in
  * de pull request daadwerkelijk verandert"). a2 + a3 + a4 + a5 of one decode step in a single
  * launch -- the same block scores, the same top-k order and selection, and the same split
  * attention and log-sum-exp merge as the separate calls above, with the steps of different
- * (sequence, KV head) units overlapping.  Block keys must be current (qsa_compress_keys first, as
- * for qsa_block_scores).
+ * (sequence, KV head) units overlapping.  As qsa_decode_scores_refresh does, the block key holding
+ * each sequence's newest token is rebuilt from K, stored and scored with (a rebuilt key must not
+ * be read by another sequence of the same call); every other block key must be current
+ * (qsa_compress_keys).
  *   sel_idx int32 [batch][Hkv][k] and sel_cnt int32 [batch][Hkv] receive the
  *     selection, exactly as qsa_topk_blocks writes it;
  *   out bf16 at out + row * out_row_stride ([Hq][256] per row, 8-byte aligned,

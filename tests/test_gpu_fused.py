@@ -283,3 +283,35 @@ def fused_counted(d: Dev, ws: torch.Tensor):
     unit = ws[256:256 + 16 * c.B * c.Hkv].view(torch.int32).cpu().numpy().reshape(-1, 4)
     assert np.all(unit[:, 0] == 0) and np.all(unit[:, 2] == 0) and np.all(unit[:, 1] == ctl[3])
     return to_np(sel), to_np(cnt), to_np(out), to_np(lse)
+
+
+@pytest.mark.parametrize("ckey_dtype,kv_dtype", [("fp32", "bf16"), ("bf16", "bf16"), ("fp8", "fp8")])
+def test_fused_rebuilds_the_newest_block_key(ckey_dtype, kv_dtype):
+    """The fused launch rebuilds the block key holding each sequence's newest token,
+    as qsa_decode_scores_refresh does: with those keys spoilt beforehand, its block-key
+    pool, selection and output equal the separate path's (refresh-and-score launch,
+    top-k, attention) bit for bit."""
+    from test_gpu_refresh import spoil_newest
+    case = small_decode("frefresh", 16, 16, 2, [4096, 4097, 4098, 4099, 1, 5, 9000], 64, jitter=True,
+                        ckey_dtype=ckey_dtype, kv_dtype=kv_dtype)
+    d = Dev(case)
+    d.compress()
+    spoil_newest(d)
+    spoiled = d.t["ckey"].clone()
+    q = d.t["q"]
+    stride = d.stride
+    s = torch.empty((case.B, case.Hkv, stride), dtype=torch.float32, device="cuda")
+    qsa.qsa_decode_scores_refresh(d.kv, q, q.stride(0), case.Hq, s, stride)
+    sel_ref, cnt_ref = d.topk(s, case.topk)
+    out_ref, lse_ref = d.decode_attn(sel_ref, cnt_ref, case.topk)
+    torch.cuda.synchronize()
+    pool_ref = d.t["ckey"].clone()
+    d.t["ckey"].copy_(spoiled)
+    fsel, fcnt, fout, flse = fused(d)
+    assert torch.equal(d.t["ckey"].view(torch.uint8), pool_ref.view(torch.uint8)), "block-key pool differs"
+    assert np.array_equal(fsel, to_np(sel_ref)) and np.array_equal(fcnt, to_np(cnt_ref))
+    check_decode_against_oracle(case, d, to_np(s), fsel, fcnt, fout, flse, case.topk)
+    ro, rl = to_np(out_ref), to_np(lse_ref)
+    for r in range(case.B):
+        check_close(fout[r], ro[r], f"fused vs separate out row {r}")
+        check_lse(flse[r], rl[r], f"fused vs separate lse row {r}")
