@@ -505,8 +505,12 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
             "new_tokens_per_s": round(case.R / dt, 1), "ms_per_chunk": round(dt * 1e3, 4),
             "tflops": round((score_flops + attn_flops) / dt / 1e12, 2),
             "event_ms": {n: round(float(m), 5) for n, m in zip(names, part_ms)},
+            # the scores run on bf16 matrix cores with each fp32 operand split into three
+            # bf16 pieces: 6 bf16 products per fp32 product (3 with bf16 or fp8 block keys)
             "scores_tflops": round(score_flops / (part_ms[1] / 1e3) / 1e12, 2),
             "scores_frac_of_fp32_matrix_peak": round(score_flops / (part_ms[1] / 1e3) / 157.3e12, 4),
+            "scores_bf16_mfma_frac": round((6 if ckey_dtype == "fp32" else 3) * score_flops / (part_ms[1] / 1e3)
+                                           / 2.5e15, 4),
             "attention_tflops": round(attn_flops / (part_ms[3] / 1e3) / 1e12, 2),
             "cold_cache_ms_per_chunk_median": cold}
 

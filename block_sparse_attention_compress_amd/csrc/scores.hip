@@ -67,21 +67,47 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
 
 // Extend: 16 rows per wave, kTiledWaves waves (64 rows) per workgroup, and
 // kTiledChunk blocks per workgroup (grid z), so a chunk of new tokens spreads
-// over every CU.  Lane
-// (c = lane & 15, kq = lane >> 4) holds, at k-step m, qsum[row c][64 kq + m] (A
-// operand) and ckey[block c][64 kq + m] (B operand): the same dim for A and B, so
-// the 64 steps of the 16x16x4 matrix-core op cover all 256 dims.  Output element
-// i of the lane is row 4 kq + i, block c of the tile.
+// over every CU.
 //
 // When the workgroup's rows belong to one sequence (the usual extend chunk), its
 // waves share each 16-block tile of keys: the threads load it together, it is
-// staged in LDS (fp32, rows padded against bank conflicts), and two tiles are in
-// flight while one is multiplied.  Otherwise each wave streams its own tiles, a
-// quarter (16 dims) at a time so that this path needs few registers, and rows of
-// one wave that belong to different sequences are scored in separate passes.
-constexpr int kTiledChunk = 512;
+// staged in LDS, and two tiles are in flight while one is multiplied.  The
+// product runs on bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with fp32
+// accuracy: every fp32 operand x is split exactly into three bf16 pieces
+// x = x1 + x2 + x3 (x1 = bf16(x), x2 = bf16(x - x1), x3 = x - x1 - x2, each step
+// exact), the products of two bf16 values are exact in fp32, and
+//   q . k = q1.k1 + (q1.k2 + q2.k1 + q1.k3 + q2.k2 + q3.k1) + (terms below 2^-24 |q||k|)
+// with the first dot product in one fp32 accumulator and the five smaller ones
+// in another, so the rounding error is that of an fp32 dot product of the same
+// length.  bf16 and fp8 block keys are exact bf16 values: one key piece, three
+// products.  Lane (c = lane & 15, kq = lane >> 4) holds, for k-slice m, dims
+// 32 m + 8 kq .. + 7 of query row c (A) and of block c of the tile (B); output
+// element i of the lane is row 4 kq + i, block c.
+//
+// Otherwise (rows of several sequences in one workgroup) each wave streams its
+// own tiles in fp32 on 16x16x4 fp32 matrix cores, a quarter (16 dims) at a time
+// so that this path needs few registers; there lane (c, kq) holds, at k-step m,
+// dims 64 kq + m of row c (A) and of block c (B).  Rows of one wave that belong
+// to different sequences are scored in separate passes.
+constexpr int kTiledChunk = 1024;
 constexpr int kTiledWaves = 4;  // waves (16 query rows each) per workgroup (8: slower)
-constexpr int kTRow = kHeadDim + 4;  // padded key row of an LDS tile (floats)
+constexpr int kSRow = kHeadDim + 8;  // padded key row of an LDS tile plane (bf16 elements)
+// pages of one sequence that a chunk's blocks can span (4-token pages: one per block)
+constexpr int kTiledPages = kTiledChunk + 1;
+
+// x -> its first N bf16 pieces (bit patterns, low 16 bits): piece 1 = bf16(x),
+// piece 2 = bf16(x - piece 1), piece 3 = bf16(x - piece 1 - piece 2).  Each
+// difference is exact in fp32, and for N = 3 the pieces sum to x exactly (an fp32
+// significand has 24 bits, a bf16 one 8); N = 1 is the plain rounding.
+template <int N>
+__device__ __forceinline__ void split_bf16(float x, uint32_t* pc) {
+    float r = x;
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+        pc[p] = f32_to_bf16_rne(r);
+        r -= __uint_as_float(pc[p] << 16);
+    }
+}
 
 template <int KT, int NW>
 __global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
@@ -89,7 +115,9 @@ __global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
     const int32_t* __restrict__ q_pos, int R, int g, const void* __restrict__ ckey,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv, int lg_ps, int max_pages,
     float* __restrict__ scores, int score_stride) {
-    __shared__ float ktile[2][16 * kTRow];
+    constexpr int NP = KT == kKeyF32 ? 3 : 1;  // bf16 pieces of a key element
+    __shared__ __attribute__((aligned(16))) uint16_t ktile[2][NP][16 * kSRow];
+    __shared__ int64_t ptab[kTiledPages];  // block-table entries of the chunk (one-sequence path)
     __shared__ int w_smin[NW], w_smax[NW], w_nend[NW];
     constexpr int TPB = 4 * NW;        // threads per block key of a staged tile
     constexpr int FPT = 64 / TPB;      // float4 (Raw) pieces per thread
@@ -140,13 +168,14 @@ __global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
     float a[64];
 #pragma unroll
     for (int m = 0; m < 64; ++m) a[m] = 0.f;
-    if (live) {
-        const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + 64 * kq;
-        for (int j = 0; j < g; ++j) {
-            const uint4* p = reinterpret_cast<const uint4*>(qrow + j * kHeadDim);
-            uint4 ws[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ws[i] = p[i];
+    // the group sum in head order; two heads' loads are in flight at a time
+    // SLICED: lane dims 32 m + 8 kq + i at a[8 m + i] (the bf16 path), else dims
+    // 64 kq + i at a[i] (the fp32 path)
+    auto sum_query = [&](bool sliced) {
+        if (!live) return;
+        const uint16_t* qrow = q + (int64_t)row * q_stride + (int64_t)h * g * kHeadDim + (sliced ? 8 : 64) * kq;
+        const int step = sliced ? 32 : 8;  // elements between the lane's 8-element pieces
+        auto add_head = [&](const uint4* ws) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint4 w = ws[i];
@@ -159,8 +188,19 @@ __global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
                 a[8 * i + 6] += bf16_lo(w.w);
                 a[8 * i + 7] += bf16_hi(w.w);
             }
+        };
+        for (int j = 0; j < g; j += 2) {
+            const uint16_t* p0 = qrow + j * kHeadDim;
+            const uint16_t* p1 = qrow + min(j + 1, g - 1) * kHeadDim;
+            uint4 w0[8], w1[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w0[i] = *reinterpret_cast<const uint4*>(p0 + step * i);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w1[i] = *reinterpret_cast<const uint4*>(p1 + step * i);
+            add_head(w0);
+            if (j + 1 < g) add_head(w1);
         }
-    }
+    };
 
     if (smin == smax) {
         // ---- shared tiles through LDS; every wave stays to the end (barriers)
@@ -172,50 +212,97 @@ __global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
         for (int i = 0; i < 4; ++i) ne_out[i] = __shfl(ne_c, 4 * kq + i);
         const int wave_end = min(wave_max_int(ne_c), bc0 + kTiledChunk);
         const int ntiles = (wg_end - bc0 + 15) / 16;
-        // this thread's share of a tile: block bl, float4 slots f0 + 16 j of its key
+        // the block-table entries of the chunk's blocks [bc0, min(wg_end, nb_seq)) go to
+        // LDS first, so that no key load waits on a dependent table load in the loop
+        if (nb_seq <= bc0) return;  // (uniform) only with a position past its sequence's end
+        const int bmax = min(wg_end, nb_seq) - 1;  // >= bc0; pages past the sequence are never read
+        const int p0 = bc0 >> lg_bpp;
+        for (int i = tid; i <= (bmax >> lg_bpp) - p0; i += 64 * NW)
+            ptab[i] = block_table[(int64_t)s * max_pages + p0 + i];
+        __syncthreads();
+        // this thread's share of a tile: block bl, float4 slots f0 + 16 j of its key.
+        // Blocks past the sequence load its last block instead: their scores are
+        // never stored (every row's eligible blocks end inside the sequence).
         const int bl = tid / TPB, f0 = tid % TPB;
         auto load = [&](int t, Raw* gr) {
-            const int b = bc0 + 16 * t + bl;
-            if (b < nb_seq) {
-                const int64_t page = block_table[(int64_t)s * max_pages + (b >> lg_bpp)];
-                const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
-                const Raw* src = keys + brow * (kHeadDim / 4) + f0;
+            const int b = min(bc0 + 16 * t + bl, bmax);
+            const int64_t page = ptab[(b >> lg_bpp) - p0];
+            const int64_t brow = ((page * Hkv + h) << lg_bpp) + (b & ((1 << lg_bpp) - 1));
+            const Raw* src = keys + brow * (kHeadDim / 4) + f0;
 #pragma unroll
-                for (int j = 0; j < FPT; ++j) gr[j] = src[TPB * j];
-            } else {
-#pragma unroll
-                for (int j = 0; j < FPT; ++j) gr[j] = Raw{};
-            }
+            for (int j = 0; j < FPT; ++j) gr[j] = src[TPB * j];
         };
+        bf16x8 qp[3][8];  // the query's three bf16 pieces, k-slice m at qp[piece][m]
+        // staging: the key elements as bf16 pieces, plane p holding piece p + 1
         auto stage = [&](int slot, const Raw* gr) {
-            float* dst = ktile[slot] + bl * kTRow + 4 * f0;
 #pragma unroll
-            for (int j = 0; j < FPT; ++j) *reinterpret_cast<float4*>(dst + 4 * TPB * j) = key4(gr[j]);
+            for (int j = 0; j < FPT; ++j) {
+                const int off = bl * kSRow + 4 * (f0 + TPB * j);
+                if (KT == kKeyBF16) {
+                    *reinterpret_cast<Raw*>(&ktile[slot][0][off]) = gr[j];  // already bf16
+                } else {
+                    const float4 x = key4(gr[j]);
+                    const float e[4] = {x.x, x.y, x.z, x.w};
+                    uint32_t w[NP][2];
+#pragma unroll
+                    for (int u = 0; u < 4; u += 2) {
+                        uint32_t pc[2][NP];
+#pragma unroll
+                        for (int v = 0; v < 2; ++v) split_bf16<NP>(e[u + v], pc[v]);
+#pragma unroll
+                        for (int pl = 0; pl < NP; ++pl) w[pl][u / 2] = pc[0][pl] | (pc[1][pl] << 16);
+                    }
+#pragma unroll
+                    for (int pl = 0; pl < NP; ++pl)
+                        *reinterpret_cast<uint2*>(&ktile[slot][pl][off]) = make_uint2(w[pl][0], w[pl][1]);
+                }
+            }
         };
         auto compute = [&](int t, int slot) {
             const int bt0 = bc0 + 16 * t;
             if (bt0 >= wave_end) return;  // this wave's rows are done (uniform per wave)
-            const float* src = ktile[slot] + c * kTRow + 64 * kq;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            floatx4 hi = {0.f, 0.f, 0.f, 0.f}, lo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float4 kv = *reinterpret_cast<const float4*>(src + 4 * i);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 0], kv.x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 1], kv.y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 2], kv.z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * i + 3], kv.w, acc, 0, 0, 0);
+            for (int m = 0; m < 8; ++m) {
+                bf16x8 kb[NP];
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl)
+                    kb[pl] = *reinterpret_cast<const bf16x8*>(&ktile[slot][pl][c * kSRow + 32 * m + 8 * kq]);
+                hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[0][m], kb[0], hi, 0, 0, 0);
+                lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[1][m], kb[0], lo, 0, 0, 0);
+                lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[2][m], kb[0], lo, 0, 0, 0);
+                if (NP == 3) {
+                    lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[0][m], kb[NP > 1 ? 1 : 0], lo, 0, 0, 0);
+                    lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[1][m], kb[NP > 1 ? 1 : 0], lo, 0, 0, 0);
+                    lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[0][m], kb[NP > 2 ? 2 : 0], lo, 0, 0, 0);
+                }
             }
             const int b = bt0 + c;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (b < ne_out[i]) scores[((int64_t)(r0 + 4 * kq + i) * Hkv + h) * score_stride + b] = acc[i];
+                if (b < ne_out[i]) scores[((int64_t)(r0 + 4 * kq + i) * Hkv + h) * score_stride + b] = hi[i] + lo[i];
         };
         // two register sets (named, so nothing is indexed across iterations) and two
         // LDS slots: tile t is multiplied from slot t % 2 while tiles t + 1 and t + 2
         // are in flight
         Raw g0[FPT], g1[FPT];
-        load(0, g0);
+        load(0, g0);  // the first key tiles fly while the group-summed query is formed
         if (ntiles > 1) load(1, g1);
+        sum_query(true);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            uint32_t w[3][4];
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                uint32_t pc[2][3];
+                split_bf16<3>(a[8 * m + i], pc[0]);
+                split_bf16<3>(a[8 * m + i + 1], pc[1]);
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) w[pl][i / 2] = pc[0][pl] | (pc[1][pl] << 16);
+            }
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) qp[pl][m] = __builtin_bit_cast(bf16x8, make_uint4(w[pl][0], w[pl][1], w[pl][2], w[pl][3]));
+        }
         stage(0, g0);
         __syncthreads();
         for (int t = 0; t < ntiles; t += 2) {
@@ -234,6 +321,7 @@ __global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
 
     // ---- rows of several sequences: each wave streams its own tiles
     if (r0 >= R || !__ballot(live)) return;
+    sum_query(false);
     uint64_t pending = __ballot(live && kq == 0) & 0xffffull;
     while (pending) {
         const int first = __builtin_ctzll(pending);

@@ -141,7 +141,8 @@ QSA_API int qsa_compress_keys(const qsa_kv_t* kv, const int32_t* first_token, in
  * a2 -- block scores.  Source: "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat de
  * pull request daadwerkelijk verandert" (the indexer scores the microblocks against the query). q:
  * bf16 rows, row r at q + r * q_row_stride (elements), heads contiguous inside a row ([Hq][256]).
- * q_seq / q_pos (int32 [R]) give each row's sequence and position; both may be NULL for decode
+ * q_seq / q_pos (int32 [R]) give each row's sequence and position (0 <= t < L of that sequence; a
+ * negative t gives the row no eligible block); both may be NULL for decode
  * (row r = sequence r at t = L_r - 1, R must equal batch).  Writes
  *   scores[(r * Hkv + h) * score_stride + b] = (sum_{j in group h} q[r][j]) . ckey[b]
  * in fp32 for b < n_elig(r) = min(t / 4 + 1, score_stride); entries at or after n_elig(r) are not

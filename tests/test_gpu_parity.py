@@ -111,6 +111,69 @@ def test_extend_scores_within_fp32_bound_mixed_sequences():
         assert np.all(np.isnan(s[r, 0, ne:]))
 
 
+def extend_scores_bound_check(case, d, s, rows=None):
+    """Every written score of the given rows within the fp32 Higham bound of the
+    fp64 oracle score; nothing written past the row's eligible blocks."""
+    cks = [d.ckey_logical(i) for i in range(case.B)]
+    rows = range(case.R) if rows is None else rows
+    worst = 0.0
+    for i in range(case.B):
+        rr = [r for r in rows if int(case.q_seq[r]) == i]
+        if not rr:
+            continue
+        ck = cks[i][0].astype(np.float64)                       # [nb][256], one KV head
+        qg = synth.bf16_to_f32(case.q[rr]).astype(np.float64)   # [n][g][256]
+        qsum = qg.sum(axis=1)
+        ref = qsum @ ck.T                                       # fp64 scores, [n][nb]
+        bound = score_bound_rows(qg, ck)
+        for j, r in enumerate(rr):
+            ne = min(int(case.q_pos[r]) // 4 + 1, d.stride)
+            err = np.abs(s[r, 0, :ne] - ref[j, :ne])
+            assert np.all(err <= bound[j, :ne]), (r, float((err - bound[j, :ne]).max()))
+            worst = max(worst, float((err / np.maximum(bound[j, :ne], 1e-300)).max()))
+            assert np.all(np.isnan(s[r, 0, ne:]))
+    return worst
+
+
+def score_bound_rows(qg, ck):
+    """score_bound for many rows: gamma_n sum_d sum_j |q_jd| |ckey_d|, n = g + 256 + 2."""
+    g = qg.shape[1]
+    n = g + ck.shape[1] + 2
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    return gamma * (np.abs(qg).sum(axis=1) @ np.abs(ck).T)
+
+
+@pytest.mark.parametrize("ckey_dtype", ["fp32", "bf16", "fp8"])
+def test_extend_scores_within_fp32_bound_one_sequence(ckey_dtype):
+    """Rows of one sequence (the shared-tile path on bf16 matrix cores with split
+    operands): every score within the fp32 bound, partial chunks and page tables of
+    4-token pages included."""
+    for page_size, L, n in ((64, 9000, 300), (4, 2100, 130)):
+        q_seq, q_pos = synth.extend_rows(L, n)
+        case = synth.make_case(f"sc1{page_size}", 41 + page_size, 12, 1, [L], page_size=page_size, q_seq=q_seq,
+                               q_pos=q_pos, ckey_dtype=ckey_dtype)
+        log(f"extend scores one sequence page_size={page_size} L={L} rows={n} ckey={ckey_dtype}")
+        d = Dev(case)
+        d.compress()
+        s = to_np(d.scores(extend=True))
+        worst = extend_scores_bound_check(case, d, s)
+        log(f"  worst |gpu - fp64| / bound = {worst:.4f}")
+
+
+def test_extend_scores_within_fp32_bound_full_chunk():
+    """All 4,096 rows x up to 8,192 blocks of the extend chunk (28,672 cached + 4,096
+    new tokens, (12,1) heads): every score within the fp32 bound of the fp64 score."""
+    case = synth.config("C4")
+    log("extend scores C4, all rows")
+    d = Dev(case)
+    case.drop_paged()
+    d.compress()
+    s = to_np(d.scores(extend=True))
+    worst = extend_scores_bound_check(case, d, s)
+    log(f"C4 scores: worst |gpu - fp64| / fp32 bound = {worst:.4f}")
+
+
 # ------------------------------------------------------------------------- a3
 
 def gpu_topk_exact(scores_np: np.ndarray, q_pos_np, k: int):
