@@ -562,7 +562,7 @@ def main():
     if len(names) > 1:
         result["configs"] = {n: records[n] for n in names[1:]}
     if not args.no_extend:
-        result["extend"] = extend_figures(max(3, args.steps // 4), args.flush, args.ckey, args.kv)
+        result["extend"] = extend_figures(max(20, args.steps // 2), args.flush, args.ckey, args.kv)
     print(json.dumps(result), flush=True)
 
 

@@ -13,7 +13,7 @@
 //
 // Work items, in ticket order (a global counter hands them out, so an item is
 // only ever taken after every item before it):
-//   scan item (u, c)   the block scores of chunk c (128 blocks) of unit u, the
+//   scan item (u, c)   the block scores of chunk c (kStreamChunk blocks) of unit u, the
 //                      code of scores_stream_kernel, stored at device scope.
 //                      The last chunk of u to finish (arrival counter) runs the
 //                      top-k of u and raises u's ready flag.

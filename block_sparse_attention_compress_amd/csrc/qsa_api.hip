@@ -374,7 +374,7 @@ int qsa_decode_fused(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, in
         return fail(QSA_ERR_INVALID_ARG, "out must be 8-byte aligned with a row stride >= Hq * 256, a multiple of 4");
     const int S = num_splits == 0 ? auto_splits((int64_t)p.batch * p.Hkv, k) : num_splits;
     const int64_t units = (int64_t)p.batch * p.Hkv;
-    const int64_t chunks = ((int64_t)p.max_seq_len + 3) / 4 / 128 + 2;
+    const int64_t chunks = ((int64_t)p.max_seq_len + 3) / 4 / 64 + 2;  // scan items of 64 blocks
     if (units * (chunks + S) > 0x7fffffff) return fail(QSA_ERR_UNSUPPORTED, "too many work items");
     const size_t need = qsa::fused_workspace_bytes(p.batch, p.Hkv, Hq, p.max_seq_len, S);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))

@@ -9,10 +9,11 @@
 
 namespace qsa {
 
-// blocks per workgroup: 4 waves x 2 groups of 16.  Smaller chunks spread the
-// rows over more workgroups (32 rows of 32K-64K tokens, 16 heads: 256 -> 128
-// took the scan from 152 to 144 us; 64 was no faster).
-constexpr int kStreamChunk = 128;
+// blocks per workgroup: 4 waves x 1 group of 16.  Smaller chunks spread the
+// rows over more workgroups; with nontemporal key loads, 32 rows of 32K-64K
+// tokens, (16,2) heads: 256 / 128 / 64 blocks took 127.8 / 124.5 / 122.5 us
+// (8 rows of 256K tokens: 167.2 / 164.1 / 163.4 us).
+constexpr int kStreamChunk = 64;
 constexpr int kGroups = kStreamChunk / 64;  // 16-block groups per wave
 
 // Scores of blocks [wb0, wb0 + 16 kGroups) ∩ [0, n_elig) of one (row, KV head):
