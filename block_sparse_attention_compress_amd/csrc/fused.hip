@@ -13,7 +13,7 @@
 //
 // Work items, in ticket order (a global counter hands them out, so an item is
 // only ever taken after every item before it):
-//   scan item (u, c)   the block scores of chunk c (kStreamChunk blocks) of unit u, the
+//   scan item (u, c)   the block scores of chunk c (stream_chunk blocks) of unit u, the
 //                      code of scores_stream_kernel, stored at device scope.
 //                      The last chunk of u to finish (arrival counter) runs the
 //                      top-k of u and raises u's ready flag.
@@ -526,6 +526,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2
         int* uc = F.unit_ctl + 4 * (int64_t)u;  // scan arrivals, ready word, attention arrivals
 
         if (scan) {
+            constexpr int kStreamChunk = stream_chunk(KT);
             const int nch = max(1, (n_elig + kStreamChunk - 1) / kStreamChunk);
             if (j >= nch) continue;  // past the row: not counted
             const int wb0 = j * kStreamChunk + wave * (kStreamChunk / 4);
@@ -721,7 +722,7 @@ hipError_t launch_fused_decode(const PagedKV& kv, const Rows& rows, int k, float
     F.ctl = reinterpret_cast<int*>(ws + l.ctl);
     F.unit_ctl = reinterpret_cast<int*>(ws + l.arrive);
     F.U = U;
-    F.C = (l.score_stride + kStreamChunk - 1) / kStreamChunk;
+    F.C = (l.score_stride + stream_chunk(kv.ckey_type) - 1) / stream_chunk(kv.ckey_type);
     F.S = S;
     F.n_items = U * (F.C + S);
     // QSA_FUSED_SPIN_LIMIT (tests of the time-out path only) shortens the bounded

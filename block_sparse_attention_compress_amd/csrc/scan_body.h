@@ -9,12 +9,15 @@
 
 namespace qsa {
 
-// blocks per workgroup: 4 waves x 1 group of 16.  Smaller chunks spread the
-// rows over more workgroups; with nontemporal key loads, 32 rows of 32K-64K
-// tokens, (16,2) heads: 256 / 128 / 64 blocks took 127.8 / 124.5 / 122.5 us
-// (8 rows of 256K tokens: 167.2 / 164.1 / 163.4 us).
-constexpr int kStreamChunk = 64;
-constexpr int kGroups = kStreamChunk / 64;  // 16-block groups per wave
+// Blocks per workgroup (4 waves, each a run of 16-block groups), by block-key
+// type.  fp32 keys: 64 (a 16-block group is 16 KiB; with nontemporal key loads,
+// 32 rows of 32K-64K tokens, (16,2) heads: 256 / 128 / 64 blocks took
+// 127.8 / 124.5 / 122.5 us, and 8 rows of 256K tokens 167.2 / 164.1 / 163.4 us).
+// bf16 and fp8 keys make a group 8 KiB and 4 KiB, and want more of them per
+// wave: 128 blocks (same workloads, 64 / 128 / 256 blocks: bf16 keys at 32 rows
+// 67.8 / 67.8 / 71.1 us, at 8 rows 94.3 / 86.1 / 85.9 us; fp8 keys at 32 rows
+// 41.9 / 36.8 / 38.2 us, at 8 rows 55.0 / 46.5 / 46.3 us).
+__host__ __device__ constexpr int stream_chunk(int kt) { return kt == kKeyF32 ? 64 : 128; }
 
 // Scores of blocks [wb0, wb0 + 16 kGroups) ∩ [0, n_elig) of one (row, KV head):
 //   srow[b] = (sum of the g query heads at qrow) . ckey[b]
@@ -73,6 +76,7 @@ __device__ __forceinline__ void scan_wave(const uint16_t* __restrict__ qrow, int
     const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
     const int lg_bpp = lg_ps - 2;  // blocks per page = page_size / 4
     // block-key rows of the wave's groups (PAGE16), looked up before any wait
+    constexpr int kGroups = stream_chunk(KT) / 64;  // 16-block groups per wave
     int64_t gbase[kGroups];
     if (PAGE16) {
 #pragma unroll

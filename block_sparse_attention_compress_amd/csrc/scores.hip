@@ -37,6 +37,7 @@ __global__ __launch_bounds__(256) void scores_stream_kernel(
     const int t = q_pos ? q_pos[row] : L - 1;
     if (t < 0) return;
     const int n_elig = min(t / 4 + 1, score_stride);
+    constexpr int kStreamChunk = stream_chunk(KT);
     const int chunk0 = blockIdx.x * kStreamChunk;
     if (chunk0 >= n_elig) return;
     const int lane = threadIdx.x & 63;
@@ -387,7 +388,8 @@ __global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
 hipError_t launch_scores_stream(const PagedKV& kv, const Rows& rows, float* scores, int score_stride, bool refresh,
                                 hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
-    dim3 grid((score_stride + kStreamChunk - 1) / kStreamChunk, kv.Hkv, rows.R);
+    const int chunk = stream_chunk(kv.ckey_type);
+    dim3 grid((score_stride + chunk - 1) / chunk, kv.Hkv, rows.R);
     const bool page16 = kv.lg_ps >= 6;
 #define QSA_SCAN(P16, KT, RF)                                                                                      \
     hipLaunchKernelGGL((scores_stream_kernel<P16, KT, RF>), grid, dim3(256), 0, st, rows.q, rows.q_stride,          \
