@@ -410,6 +410,29 @@ int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
                       "qsa_sparse_attn_extend");
 }
 
+int qsa_sparse_attn_extend_union(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
+                                 const int32_t* q_pos, int32_t R, int32_t Hq, const int32_t* sel_idx,
+                                 const int32_t* sel_cnt, int32_t k, float scale, void* out, int64_t out_row_stride,
+                                 float* lse, void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, true, true, false, &p)) return rc;
+    if (int rc = check_heads(Hq, p.Hkv)) return rc;
+    if (int rc = check_q(q, q_row_stride, Hq)) return rc;
+    if (!q_seq || !q_pos) return fail(QSA_ERR_INVALID_ARG, "q_seq / q_pos is NULL");
+    if (R < 0) return fail(QSA_ERR_INVALID_ARG, "R %d < 0", R);
+    if ((int64_t)R * p.Hkv > 0x7fffffff) return fail(QSA_ERR_UNSUPPORTED, "R * Hkv exceeds 2^31 - 1");
+    if (k < 0 || k > QSA_MAX_TOPK) return fail(QSA_ERR_INVALID_ARG, "k %d out of [0, %d]", k, QSA_MAX_TOPK);
+    if (!sel_cnt || (k > 0 && !sel_idx)) return fail(QSA_ERR_INVALID_ARG, "sel_idx / sel_cnt is NULL");
+    if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
+    if (out_row_stride < (int64_t)Hq * QSA_HEAD_DIM)
+        return fail(QSA_ERR_INVALID_ARG, "out_row_stride %lld < Hq * 256", (long long)out_row_stride);
+    const float sc = scale > 0.f ? scale : 0.0625f;
+    qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, q_seq, q_pos, R, Hq};
+    return hip_status(qsa::launch_attn_union(p, rows, sel_idx, sel_cnt, k, sc, static_cast<uint16_t*>(out),
+                                             out_row_stride, lse, static_cast<hipStream_t>(stream)),
+                      "qsa_sparse_attn_extend_union");
+}
+
 int qsa_merge_lse(const float* part_out, const float* part_lse, int32_t S, int32_t N, int32_t D, void* out_bf16,
                   float* out_lse, void* stream) {
     if (!part_out || !part_lse || !out_bf16) return fail(QSA_ERR_INVALID_ARG, "part_out / part_lse / out is NULL");

@@ -58,6 +58,11 @@ struct AttnOut {
 hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt, int k,
                        float scale, int num_splits, bool blocked, const AttnOut& o, hipStream_t st);
 
+// Extend attention over the union of each tile of consecutive rows' selections
+// (same result set as launch_attn with one split; outputs bf16 out, lse)
+hipError_t launch_attn_union(const PagedKV& kv, const Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt, int k,
+                             float scale, uint16_t* out, int64_t out_stride, float* lse, hipStream_t st);
+
 // Fused decode (scores, top-k, attention, merge in one persistent launch) with S
 // attention splits per (row, KV head); workspace laid out by fused_workspace_bytes,
 // its first fused_control_bytes zero before the call and zero after it.

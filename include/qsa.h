@@ -322,6 +322,24 @@ QSA_API int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_
                            float* lse, void* stream);
 
 /*
+ * a6, query-tile union -- the same attention as qsa_sparse_attn_extend (same arguments, same
+ * result set T per row, outputs within rounding of it: only the order in which a row's tokens are
+ * summed differs), computed per tile of 8 consecutive query rows and KV head over the union of the
+ * tile's selections: each selected block is read from the cache once per tile, into LDS, and used
+ * there by every row of the tile that selected it; a row's unselected or invisible tokens are
+ * masked.  Source: the per-row sets of "Qwen4-Exp QSA komt naar Huawei's Ascend", section "Wat de
+ * pull request daadwerkelijk toevoegt", and the selection of "Qwen 4 QSA krijgt
+ * decode-contextparallellisme", section "Wat de pull request daadwerkelijk verandert"; the tiling
+ * is this library's.  Rows of a tile may belong to different sequences (each sequence of a tile is
+ * a pass of its own).  It reads fewer cache bytes than the per-row kernel when adjacent rows
+ * share selected blocks, and does more masked matrix-core work when they do not.
+ */
+QSA_API int qsa_sparse_attn_extend_union(const qsa_kv_t* kv, const void* q, int64_t q_row_stride,
+                                         const int32_t* q_seq, const int32_t* q_pos, int32_t R, int32_t Hq,
+                                         const int32_t* sel_idx, const int32_t* sel_cnt, int32_t k, float scale,
+                                         void* out, int64_t out_row_stride, float* lse, void* stream);
+
+/*
  * a5 -- log-sum-exp merge of S partial results.  Source: "Qwen 4 QSA krijgt
  * decode-contextparallellisme", section "Wat de pull request daadwerkelijk verandert" (the
  * attention results of the split read are combined at the end) and its question "Hoe verschilt

@@ -41,7 +41,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 # stream ids (upper 32 bits of the stream number; the lower 32 bits hold the sequence)
-S_K, S_V, S_Q, S_LEN, S_PERM, S_KJIT, S_VJIT, S_BIAS = 1, 2, 3, 4, 5, 6, 7, 8
+S_K, S_V, S_Q, S_LEN, S_PERM, S_KJIT, S_VJIT, S_BIAS, S_QBASE = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 def build(verbose: bool = False) -> str:
@@ -167,6 +167,7 @@ class Case:
     shared_prefix_pages: int = 0     # sequence i>0 reuses the first pages of sequence 0
     ckey_dtype: str = "fp32"         # storage of the block keys: "fp32", "bf16" or "fp8"
     kv_dtype: str = "bf16"           # storage of K and V: "bf16", or "fp8" (E4M3 codes of the bf16 draws)
+    q_share: float = 0.0             # > 0: each query row is sqrt(q_share) parts a vector its sequence's rows share
     block_table: np.ndarray = field(default=None, repr=False)   # int32 [B][max_pages]
     num_pages: int = 0
     _q: Optional[np.ndarray] = field(default=None, repr=False)
@@ -198,9 +199,18 @@ class Case:
     # -------------------------------------------------------------- queries
     @property
     def q(self) -> np.ndarray:
-        """bf16 bit patterns [R][Hq][D]."""
+        """bf16 bit patterns [R][Hq][D].  N(0,1) per element; with q_share = s > 0 each
+        row is sqrt(s) * (its sequence's shared N(0,1) vector) + sqrt(1 - s) * (its own
+        N(0,1) draw), rounded to bf16, so that the rows of a sequence select overlapping
+        blocks."""
         if self._q is None:
-            self._q = normal_bf16(self.seed, S_Q, 0, (self.R, self.Hq, self.D))
+            q = normal_bf16(self.seed, S_Q, 0, (self.R, self.Hq, self.D))
+            if self.q_share > 0.0:
+                base = bf16_to_f32(normal_bf16(self.seed, S_QBASE, 0, (self.B, self.Hq, self.D))).astype(np.float64)
+                own = bf16_to_f32(q).astype(np.float64)
+                mix = np.sqrt(self.q_share) * base[self.q_seq] + np.sqrt(1.0 - self.q_share) * own
+                q = f32_to_bf16(mix.astype(np.float32))
+            self._q = q
         return self._q
 
     # ----------------------------------------------------------------- bias
@@ -343,7 +353,7 @@ def _block_table(seed: int, lens: np.ndarray, page_size: int, shuffle: bool, sha
 def make_case(name: str, seed: int, Hq: int, Hkv: int, lens, page_size: int, *, q_seq=None, q_pos=None,
               topk: int = 512, scale: float = 1.0 / 16.0, splits: int = 1, jitter: bool = False,
               bias_frac: float = 0.0, shuffle: bool = True, shared_prefix_pages: int = 0, D: int = 256,
-              ckey_dtype: str = "fp32", kv_dtype: str = "bf16") -> Case:
+              ckey_dtype: str = "fp32", kv_dtype: str = "bf16", q_share: float = 0.0) -> Case:
     lens = np.asarray(lens, dtype=np.int32)
     if q_seq is None:  # decode: one row per sequence at its last position
         q_seq = np.arange(lens.shape[0], dtype=np.int32)
@@ -353,7 +363,7 @@ def make_case(name: str, seed: int, Hq: int, Hkv: int, lens, page_size: int, *, 
                 q_seq=np.asarray(q_seq, dtype=np.int32), q_pos=np.asarray(q_pos, dtype=np.int32), topk=topk,
                 scale=scale, splits=splits, D=D, jitter=jitter, bias_frac=bias_frac, shuffle=shuffle,
                 shared_prefix_pages=shared_prefix_pages, block_table=bt, num_pages=num_pages, ckey_dtype=ckey_dtype,
-                kv_dtype=kv_dtype)
+                kv_dtype=kv_dtype, q_share=q_share)
 
 
 def uniform_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
@@ -369,9 +379,10 @@ def extend_rows(total: int, new: int, seq: int = 0):
 # ------------------------------------------------------------------ the five workloads
 
 def config(name: str, *, B: Optional[int] = None, L: Optional[int] = None, L_range=None,
-           new: Optional[int] = None) -> Case:
+           new: Optional[int] = None, q_share: float = 0.0) -> Case:
     """The named workload, optionally shrunk (fewer sequences / shorter contexts) with
-    the same recipe otherwise."""
+    the same recipe otherwise.  q_share (extend only) mixes a per-sequence shared
+    component into the queries (Case.q)."""
     if name == "C1":
         L1 = L or 8192
         return make_case("C1", 1, 16, 2, [L1] * (B or 1), page_size=L1, shuffle=False)
@@ -385,7 +396,8 @@ def config(name: str, *, B: Optional[int] = None, L: Optional[int] = None, L_ran
         total = L or 32768
         n_new = new or 4096
         q_seq, q_pos = extend_rows(total, n_new)
-        return make_case("C4", 4, 12, 1, [total], page_size=total, q_seq=q_seq, q_pos=q_pos, shuffle=False)
+        return make_case("C4", 4, 12, 1, [total], page_size=total, q_seq=q_seq, q_pos=q_pos, shuffle=False,
+                         q_share=q_share)
     if name == "C5":
         lo, hi = L_range or (65536, 131072)
         return make_case("C5", 5, 6, 1, uniform_lengths(5, B or 64, lo, hi), page_size=64, splits=4)

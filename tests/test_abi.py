@@ -204,6 +204,14 @@ def test_extend_and_merge_reject():
     assert f(ctypes.byref(d), P, 4096, None, P, 10, 16, P, P, 512, 0.0, P, 4096, None, None) == qsa.QSA_ERR_INVALID_ARG
     assert f(ctypes.byref(d), P, 4096, P, P, -1, 16, P, P, 512, 0.0, P, 4096, None, None) == qsa.QSA_ERR_INVALID_ARG
     assert f(ctypes.byref(d), P, 4096, P, P, 10, 48, P, P, 512, 0.0, P, 48 * 256, None, None) == qsa.QSA_ERR_UNSUPPORTED
+    u = qsa.lib().qsa_sparse_attn_extend_union  # same argument checks, all before any launch
+    assert u(ctypes.byref(d), P, 4096, None, P, 10, 16, P, P, 512, 0.0, P, 4096, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert u(ctypes.byref(d), P, 4096, P, P, -1, 16, P, P, 512, 0.0, P, 4096, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert u(ctypes.byref(d), P, 4096, P, P, 10, 48, P, P, 512, 0.0, P, 48 * 256, None, None) == qsa.QSA_ERR_UNSUPPORTED
+    assert u(ctypes.byref(d), P, 4096, P, P, 10, 16, P, P, 4096, 0.0, P, 4096, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert u(ctypes.byref(d), P, 4096, P, P, 10, 16, P, P, 512, 0.0, None, 4096, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert u(ctypes.byref(d), P, 4096, P, P, 10, 16, P, P, 512, 0.0, P, 1024, None, None) == qsa.QSA_ERR_INVALID_ARG
+    assert "out_row_stride" in qsa.qsa_last_error()
     m = qsa.lib().qsa_merge_lse
     assert m(P, P, 0, 10, 256, P, None, None) == qsa.QSA_ERR_INVALID_ARG
     assert m(P, P, 65, 10, 256, P, None, None) == qsa.QSA_ERR_INVALID_ARG
