@@ -64,9 +64,15 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
     typedef typename KVRaw<KV8>::type Raw;  // 8 elements of a row
     constexpr int RB = kTileRowBytes<KV8>;  // bytes of a staged row
     constexpr int EB = KV8 ? 1 : 2;         // bytes per element
-    __shared__ uint32_t bm[kUT][kUWords];   // row w chose window block j: bit j of bm[w]
-    __shared__ int32_t ublk[kUWin];         // union blocks of the window, ascending
-    __shared__ __attribute__((aligned(16))) uint8_t stage[2][2][4 * kUG * RB];  // [buffer][K, V][token row]
+    // K/V staging: [buffer][K, V][token row].  While a window is set up, its first
+    // bytes hold the rows' membership bitmaps and the union list instead.
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2][2][4 * kUG * RB];
+    static_assert(sizeof(stage) >= (size_t)(kUT * kUWords + kUWin) * 4, "setup arrays fit the staging space");
+    uint32_t (*bm)[kUWords] = reinterpret_cast<uint32_t (*)[kUWords]>(&stage[0][0][0]);  // row w chose block j
+    int32_t* ublk = reinterpret_cast<int32_t*>(&stage[0][0][0]) + kUT * kUWords;       // union, ascending
+    __shared__ int32_t ubase[kUWin];        // union block i: K/V row of its first token
+    __shared__ uint16_t gmask[kUT][kUWin / kUG];  // row w: which blocks of union group gi it chose
+    __shared__ int rdiag[kUT];              // row w: union index of its partly visible block, or -1
     __shared__ int rseq[kUT], rvis[kUT];    // per row: sequence (-1: none), last visible position
     __shared__ int wsum[kUThreads / 64];
     __shared__ int sh_nu;
@@ -173,19 +179,40 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
                 __syncthreads();
             }
             const int nu = sh_nu;
+            const int ngrp = (nu + kUG - 1) / kUG;
+            // ---- the union blocks' K/V rows, and per row and group the chosen blocks
+            if (tid < kUT) rdiag[tid] = -1;
+            __syncthreads();
+            for (int e = tid; e < nu; e += kUThreads)
+                ubase[e] = (int32_t)token_row(P.block_table, sq, P.max_pages, P.Hkv, h, P.lg_ps, 4 * (int64_t)ublk[e]);
+            for (int e = tid; e < kUT * ngrp; e += kUThreads) {
+                const int w = e / ngrp, gi = e % ngrp;
+                const int dblk = rseq[w] == sq && rvis[w] >= 0 ? rvis[w] >> 2 : -1;  // block holding t
+                uint32_t msk = 0;
+                for (int j = 0; j < kUG; ++j) {
+                    const int ui = kUG * gi + j;
+                    if (ui >= nu) break;
+                    const int b = ublk[ui];
+                    if ((bm[w][(b - w0) >> 5] >> ((b - w0) & 31)) & 1u) {
+                        msk |= 1u << j;
+                        if (b == dblk) rdiag[w] = ui;
+                    }
+                }
+                gmask[w][gi] = (uint16_t)msk;
+            }
+            __syncthreads();
+            const int my_diag = rdiag[wave];
+            const int diag_live = (2 << (my_vis & 3)) - 1;  // its tokens up to t
 
             // ---- 3. groups of kUG union blocks (4 kUG token rows) staged in LDS
-            const int ngrp = (nu + kUG - 1) / kUG;
-            // this thread's K/V row piece p of group gi (token row ts + 16 p; masked or
-            // past the end: row 0).  The block table is read here, a group ahead.
+            // this thread's K/V row piece p of group gi (token row ts + 16 p; past the
+            // end of the union: row 0)
             auto issue1 = [&](int gi, int p, Raw& kr, Raw& vr) {
                 const int tr = ts + 16 * p;
                 const int ui = kUG * gi + (tr >> 2);
-                int64_t rr = 0;
-                if (ui < nu) {
-                    const int64_t pos = 4 * (int64_t)ublk[ui] + (tr & 3);
-                    if (pos < L) rr = token_row(P.block_table, sq, P.max_pages, P.Hkv, h, P.lg_ps, pos);
-                }
+                // a block's 4 rows lie in one page, so the rows of its tokens at or past L
+                // exist too (they are masked)
+                const int64_t rr = ui < nu ? (int64_t)ubase[ui] + (tr & 3) : 0;
                 const int64_t off = rr * kHeadDim * EB + (int64_t)sizeof(Raw) * pc;
                 kr = *reinterpret_cast<const Raw*>(kbytes + off);
                 vr = *reinterpret_cast<const Raw*>(vbytes + off);
@@ -212,17 +239,8 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
             // group gi from staging buffer buf, for this wave's row: its member blocks
             // of the group, 4 at a time (16 tokens), gathered from the staged rows
             auto compute = [&](int gi, int buf) {
-                // member mask over the group's blocks, from lanes 0 .. kUG - 1
-                int mb = -1;  // lane l < kUG: the group's block l
-                bool member = false;
-                if (mine && lane < kUG) {
-                    const int ui = kUG * gi + lane;
-                    if (ui < nu) {
-                        mb = ublk[ui];
-                        member = (bm[wave][(mb - w0) >> 5] >> ((mb - w0) & 31)) & 1u;
-                    }
-                }
-                const uint32_t mask = (uint32_t)__ballot(member);
+                // the group's blocks this row chose (bit j: union block kUG gi + j)
+                const uint32_t mask = mine ? gmask[wave][gi] : 0u;
                 const int nm = __popc(mask);
                 if (nm == 0) return;  // wave-uniform
                 // lane l < nm: the group slot of member l (the l-th set bit of mask)
@@ -238,15 +256,11 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
                     // K operand: token c of the tile = token c & 3 of member j0 + c / 4
                     const int sk = __shfl(slot, min(j0 + (c >> 2), nm - 1));
                     const uint8_t* krow = ktile + (4 * sk + (c & 3)) * RB;
-                    // this lane's tokens 4 qq + i: member j0 + qq
+                    // this lane's tokens 4 qq + i: member j0 + qq, all visible unless it is
+                    // the block holding t
                     const int jm = j0 + qq;
                     const int sv = __shfl(slot, min(jm, nm - 1));
-                    const int bv = __shfl(mb, sv);
-                    int live = 0;
-                    if (jm < nm) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) live |= (int)(4 * (int64_t)bv + i <= my_vis) << i;
-                    }
+                    const int live = jm < nm ? (kUG * gi + sv == my_diag ? diag_live : 15) : 0;
                     floatx4 st = {0.f, 0.f, 0.f, 0.f};
                     {
                         bf16x8 kb[8];
