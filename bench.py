@@ -497,6 +497,20 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
     # matrix-core work: scores 2*256 per eligible block per row; attention 2 * 2 * 256
     # per (selected token, real head)
     elig = sum(min(int(t) // 4 + 1, stride) for t in case.q_pos)
+    # the query-tile union kernel on the same selection (an alternative entry point, timed beside)
+    uo = torch.empty_like(buf.out)
+    ul = torch.empty_like(buf.lse)
+    union = lambda: qsa.qsa_sparse_attn_extend_union(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.sel_idx,
+                                                     buf.sel_cnt, 512, case.scale, uo, uo.stride(0), ul)
+    union()
+    torch.cuda.synchronize()
+    ut = Timer(steps, 2)
+    for i in range(steps):
+        ut.ev[i][0].record()
+        union()
+        ut.ev[i][1].record()
+    torch.cuda.synchronize()
+    union_ms = float(ut.ms().mean(axis=0)[0])
     cnt = buf.sel_cnt.cpu().numpy()
     score_flops = 2 * 256 * elig
     attn_flops = 4 * 256 * case.Hq * int(cnt.sum()) * 4
@@ -512,6 +526,7 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
             "scores_bf16_mfma_frac": round((6 if ckey_dtype == "fp32" else 3) * score_flops / (part_ms[1] / 1e3)
                                            / 2.5e15, 4),
             "attention_tflops": round(attn_flops / (part_ms[3] / 1e3) / 1e12, 2),
+            "union_attention_event_ms": round(union_ms, 5),
             "cold_cache_ms_per_chunk_median": cold}
 
 
