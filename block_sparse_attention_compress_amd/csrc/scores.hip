@@ -7,7 +7,7 @@
 // KV head).  Scores are left unscaled: the softmax scale does not change the
 // order.
 //
-// Two kernels, both fp32:
+// Two kernels, both with fp32 results:
 //  * scores_stream_kernel (decode): one row reads its whole block-key list once.
 //    This is the dominant HBM stream of a decode step.  A wave takes 16 blocks
 //    (16 KiB of fp32 keys; 8 KiB bf16, 4 KiB fp8) at a time, each lane 4 dims of
@@ -16,8 +16,10 @@
 //    rebuilds the block key of each sequence's newest token from K (bf16 or fp8
 //    rows) and scores that block with it, replacing a separate compress launch.
 //  * scores_tiled_kernel (extend): many query rows share one sequence, so the
-//    scores are a dense [rows x 256] . [256 x blocks] product; 16x16x4 fp32
-//    matrix-core tiles, 16 rows per wave.
+//    scores are a dense [rows x 256] . [256 x blocks] product, 16 rows per wave:
+//    bf16 matrix cores with exact three-way bf16 splits of the fp32 operands
+//    (fp32 accuracy, below), or 16x16x4 fp32 matrix cores when a workgroup's
+//    rows belong to several sequences.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 #include "scan_body.h"
