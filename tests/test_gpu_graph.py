@@ -1,6 +1,6 @@
-"""A decode step, and an extend chunk, captured in a HIP graph replay to the same
-bits as the eager calls, on several replays with eager work and synchronisations in
-between."""
+"""A decode step, an extend chunk, and the query-tile union attention, captured in a
+HIP graph replay to the same bits as the eager calls, on several replays with eager
+work and synchronisations in between."""
 import numpy as np
 import pytest
 import torch
@@ -101,4 +101,46 @@ def test_extend_chunk_graph_replays_match_eager(kv_dtype):
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
         chunk()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_union_extend_attention_graph_replays_match_eager():
+    """The query-tile union kernel captured after the extend chunk's selection: each
+    replay's outputs equal the eager call's bit for bit, with eager work between."""
+    total, new = 6000, 300
+    q_seq, q_pos = synth.extend_rows(total, new)
+    case = synth.make_case("ugraph", 62, 16, 2, [total], page_size=64, q_seq=q_seq, q_pos=q_pos, q_share=0.5)
+    log("union extend attention graph replay")
+    dev = synth.to_device(case, "cuda")
+    kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
+    qsa.qsa_compress_keys(kv)
+    stride = case.nb(0)
+    buf = ExtendBuffers.allocate(case.R, case.Hq, case.Hkv, stride, case.topk, "cuda")
+    extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, scale=case.scale)
+    q = dev["q"]
+
+    def union():
+        qsa.qsa_sparse_attn_extend_union(kv, q, q.stride(0), dev["q_seq"], dev["q_pos"], case.R, case.Hq, buf.sel_idx,
+                                         buf.sel_cnt, case.topk, case.scale, buf.out, buf.out.stride(0), buf.lse)
+
+    union()
+    torch.cuda.synchronize()
+    want = (buf.out.clone(), buf.lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        union()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        union()
+    for rep in range(4):
+        buf.out.fill_(float("nan"))
+        buf.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((buf.out, buf.lse), want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+        union()  # eager work between replays
         torch.cuda.synchronize()
