@@ -17,16 +17,18 @@
 // exchange or merge between waves is needed.  Per sequence present in the tile
 // and per window of kUWin blocks:
 //   1. membership bitmaps, one per row, from the rows' selections (LDS atomics);
-//   2. their union, compacted in ascending block order, and each union block's
-//      first K/V row from the block table;
-//   3. 16-token chunks (4 union blocks) staged in LDS -- the loads of the next
-//      kUDepth chunks in flight in registers, two staging buffers, one barrier
-//      per chunk -- and each wave runs the chunk's tokens through the same
-//      matrix-core tile as the per-row kernel (S^T = K Q^T on
-//      v_mfma_f32_16x16x32_bf16, lazy-rescaled online softmax in base 2, P
-//      rounded to bf16, O += P V on v_mfma_f32_16x16x16bf16_1k), with the
-//      tokens its row did not select, or cannot see, masked.  A wave skips a
-//      chunk holding none of its row's tokens.
+//   2. their union, compacted in ascending block order;
+//   3. each union block's first K/V row from the block table, and per row and
+//      group of kUG union blocks a mask of the blocks the row chose;
+//   4. groups of kUG union blocks (4 kUG token rows) staged in LDS -- the next
+//      group's loads in flight in registers, two staging buffers, one barrier
+//      per group -- and each wave runs its own members of the group, 4 blocks
+//      (16 tokens) at a time, through the same matrix-core tile as the per-row
+//      kernel (S^T = K Q^T on v_mfma_f32_16x16x32_bf16, lazy-rescaled online
+//      softmax in base 2, P rounded to bf16, O += P V on
+//      v_mfma_f32_16x16x16bf16_1k), reading the operands from the staged rows by
+//      per-lane address.  Only a row's last tile of a group and its partly
+//      visible block carry masked tokens.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 #include "attn_body.h"
@@ -133,7 +135,6 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
         bool seen = false;
         for (int j = 0; j < pass; ++j) seen |= rseq[j] == sq;
         if (seen) continue;
-        const int L = P.seq_lens[sq];
         int nb = 0;  // blocks holding a token visible to some row of this sequence
         for (int j = 0; j < kUT; ++j)
             if (rseq[j] == sq && rvis[j] >= 0) nb = max(nb, rvis[j] / 4 + 1);
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
             }
             const int nu = sh_nu;
             const int ngrp = (nu + kUG - 1) / kUG;
-            // ---- the union blocks' K/V rows, and per row and group the chosen blocks
+            // ---- 3. the union blocks' K/V rows, and per row and group the chosen blocks
             if (tid < kUT) rdiag[tid] = -1;
             __syncthreads();
             for (int e = tid; e < nu; e += kUThreads)
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
             const int my_diag = rdiag[wave];
             const int diag_live = (2 << (my_vis & 3)) - 1;  // its tokens up to t
 
-            // ---- 3. groups of kUG union blocks (4 kUG token rows) staged in LDS
+            // ---- 4. groups of kUG union blocks (4 kUG token rows) staged in LDS
             // this thread's K/V row piece p of group gi (token row ts + 16 p; past the
             // end of the union: row 0)
             auto issue1 = [&](int gi, int p, Raw& kr, Raw& vr) {
