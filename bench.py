@@ -86,6 +86,9 @@ def parse():
                    help="also time single steps after a 1 GiB read that evicts the caches (MALL included)")
     p.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                    help="main cache storage (bf16; fp8: E4M3 codes of the same draws)")
+    p.add_argument("--q-share", type=float, default=0.0,
+                   help="extend only: queries share a per-sequence component with this weight (0.9: 8 adjacent rows "
+                        "select a quarter as many distinct blocks as 8 x 512), for the query-tile union kernel")
     p.add_argument("--ckey", choices=["fp32", "bf16", "fp8"], default="fp32",
                    help="block-key storage (fp32: the method's definition; bf16 / fp8: the rounded-mean variants)")
     return p.parse_args()
@@ -437,7 +440,8 @@ def decode_record(name: str, args, headline: bool) -> dict:
     return rec
 
 
-def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv_dtype: str = "bf16"):
+def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv_dtype: str = "bf16",
+                   q_share: float = 0.0):
     """Extend chunk: 4096 new query tokens on 28672 cached (32768 total), (12, 1) heads."""
     import numpy as np
     import torch
@@ -446,7 +450,7 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
     import synth
     from block_sparse_attention_compress_amd.pipeline import ExtendBuffers, extend_step
 
-    case = synth.config("C4")
+    case = synth.config("C4", q_share=q_share)
     case.ckey_dtype, case.kv_dtype = ckey_dtype, kv_dtype
     dev = synth.to_device(case, "cuda")
     kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
@@ -515,7 +519,8 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
     score_flops = 2 * 256 * elig
     attn_flops = 4 * 256 * case.Hq * int(cnt.sum()) * 4
     return {"workload": f"extend: 4096 new tokens on 28672 cached, (12,1) heads, top-512 per query, "
-                        f"{kv_dtype} K/V, {ckey_dtype} block keys",
+                        f"{kv_dtype} K/V, {ckey_dtype} block keys"
+                        + (f", queries with a shared per-sequence component (weight {q_share})" if q_share else ""),
             "new_tokens_per_s": round(case.R / dt, 1), "ms_per_chunk": round(dt * 1e3, 4),
             "tflops": round((score_flops + attn_flops) / dt / 1e12, 2),
             "event_ms": {n: round(float(m), 5) for n, m in zip(names, part_ms)},
@@ -543,7 +548,7 @@ def main():
         return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.extend_only:
-        print(json.dumps(extend_figures(args.steps, args.flush, args.ckey, args.kv)), flush=True)
+        print(json.dumps(extend_figures(args.steps, args.flush, args.ckey, args.kv, args.q_share)), flush=True)
         return
     import block_sparse_attention_compress_amd as qsa
 
