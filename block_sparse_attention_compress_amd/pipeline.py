@@ -13,7 +13,8 @@ import torch
 
 from . import (HEAD_DIM, KVCache, qsa_block_scores, qsa_compress_keys, qsa_decode_fused, qsa_decode_scores_refresh,
                qsa_decode_fused_workspace_bytes, qsa_decode_workspace_bytes, qsa_sparse_attn_decode,
-               qsa_sparse_attn_extend, qsa_topk_blocks, qsa_topk_blocks_ws, qsa_topk_workspace_bytes)
+               qsa_sparse_attn_extend, qsa_sparse_attn_extend_union, qsa_topk_blocks, qsa_topk_blocks_ws,
+               qsa_topk_workspace_bytes)
 
 
 @dataclass
@@ -126,17 +127,19 @@ class ExtendBuffers:
 
 def extend_step(kv: KVCache, q: torch.Tensor, q_seq: torch.Tensor, q_pos: torch.Tensor, buf: ExtendBuffers,
                 first_new: Optional[torch.Tensor] = None, max_new_tokens: int = 0, scale: float = 0.0,
-                stream=None) -> None:
+                stream=None, union_tiles: bool = False) -> None:
     """One extend chunk: block keys of the new tokens (first_new [B] = first new
-    position per sequence), then per-row scores, selection and attention."""
+    position per sequence), then per-row scores, selection and attention (with
+    union_tiles, the query-tile union kernel: the same result sets, usually slower)."""
     R, Hq = q.shape[0], q.shape[1]
     Hkv = kv.k.shape[1]
     if first_new is not None:
         qsa_compress_keys(kv, first_new, max_new_tokens, stream=stream)
     qsa_block_scores(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.scores, buf.score_stride, stream=stream)
     qsa_topk_blocks(buf.scores, buf.score_stride, q_pos, R, Hkv, buf.k, buf.sel_idx, buf.sel_cnt, stream=stream)
-    qsa_sparse_attn_extend(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale, buf.out,
-                           buf.out.stride(0), buf.lse, stream=stream)
+    attend = qsa_sparse_attn_extend_union if union_tiles else qsa_sparse_attn_extend
+    attend(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale, buf.out, buf.out.stride(0),
+           buf.lse, stream=stream)
 
 
 class DecodeGraph:

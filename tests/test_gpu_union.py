@@ -169,3 +169,20 @@ def test_union_strided_query_and_output_rows():
     assert torch.all(obig[:, case.Hq:] == 7.0)
     assert torch.equal(ov.contiguous().view(torch.int16), o1.view(torch.int16))
     assert torch.equal(l2.view(torch.int32), l1.view(torch.int32))
+
+
+def test_union_through_the_extend_step():
+    """extend_step(..., union_tiles=True) gives the direct union call's outputs bit for bit."""
+    from block_sparse_attention_compress_amd.pipeline import ExtendBuffers, extend_step
+    total, nq = 5000, 61
+    q_seq, q_pos = synth.extend_rows(total, nq)
+    case = synth.make_case("union-step", 614, 24, 2, [total], page_size=64, q_seq=q_seq, q_pos=q_pos, q_share=0.5)
+    dev, kv = upload(case)
+    qsa.qsa_compress_keys(kv)
+    buf = ExtendBuffers.allocate(case.R, case.Hq, case.Hkv, case.nb(0), case.topk, "cuda")
+    extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, scale=case.scale, union_tiles=True)
+    out, lse = union_attn(kv, dev["q"], dev["q_seq"], dev["q_pos"], case.R, case.Hq, buf.sel_idx, buf.sel_cnt,
+                          case.topk, case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.out.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(buf.lse.view(torch.int32), lse.view(torch.int32))
