@@ -227,6 +227,40 @@ def cpu_baseline(case, target_s: float, max_rows: int):
             "host_threads": threads, "cpu_model": cpu_model()}
 
 
+def extend_cpu_baseline(case, target_s: float, nrows: int = 128):
+    """The CPU oracle on a sample of the extend chunk's rows (rows spread evenly over
+    the chunk), all host threads; and a short single-thread sample."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    rows = [int(r) for r in np.linspace(0, case.R - 1, nrows).round()]
+    data = oracle.CaseData(case)
+    data.prefetch([0], threads)  # logical K and block keys: not timed
+    data.V(0)
+
+    def timed(rows_, nthreads, span):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.run_case(case, rows=rows_, threads=nthreads, data=data, keep_scores=False)
+            reps += 1
+            if time.perf_counter() - t0 >= span:
+                break
+        return reps, time.perf_counter() - t0
+
+    reps, dt = timed(rows, threads, target_s)
+    reps1, dt1 = timed(rows[:8], 1, max(1.0, target_s / 4))
+    return {"value": round(reps * len(rows) / dt, 3), "unit": "new tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle extend rows (scores, top-{case.topk}, causal attention) for {len(rows)} of the "
+                      f"chunk's {case.R} new tokens, spread evenly over it, on {threads} threads, {reps} repetitions "
+                      f"in {dt:.2f} s, block keys precomputed",
+            "single_thread_value": round(reps1 * 8 / dt1, 3),
+            "single_thread_sample": f"8 of those rows on 1 thread, {reps1} repetitions in {dt1:.2f} s",
+            "host_threads": threads, "cpu_model": cpu_model()}
+
+
 def traffic_record(case):
     """HBM bytes per launch of the scan from the committed PMC summary of this
     workload, or None when the scan's sources changed since it was taken."""
@@ -441,7 +475,7 @@ def decode_record(name: str, args, headline: bool) -> dict:
 
 
 def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv_dtype: str = "bf16",
-                   q_share: float = 0.0):
+                   q_share: float = 0.0, cpu_seconds: float = 0.0):
     """Extend chunk: 4096 new query tokens on 28672 cached (32768 total), (12, 1) heads."""
     import numpy as np
     import torch
@@ -532,7 +566,8 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
                                            / 2.5e15, 4),
             "attention_tflops": round(attn_flops / (part_ms[3] / 1e3) / 1e12, 2),
             "union_attention_event_ms": round(union_ms, 5),
-            "cold_cache_ms_per_chunk_median": cold}
+            "cold_cache_ms_per_chunk_median": cold,
+            "cpu_baseline": extend_cpu_baseline(case, cpu_seconds) if cpu_seconds > 0 else None}
 
 
 def main():
@@ -582,7 +617,8 @@ def main():
     if len(names) > 1:
         result["configs"] = {n: records[n] for n in names[1:]}
     if not args.no_extend:
-        result["extend"] = extend_figures(max(20, args.steps // 2), args.flush, args.ckey, args.kv)
+        result["extend"] = extend_figures(max(20, args.steps // 2), args.flush, args.ckey, args.kv,
+                                          cpu_seconds=0.0 if args.no_cpu_baseline else 0.4 * args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
