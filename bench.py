@@ -573,7 +573,7 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
               f"run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
