@@ -40,7 +40,7 @@
 namespace qsa {
 
 template <bool KV8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(const AttnParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 2, 8))) void attn_kernel(const AttnParams P) {
     extern __shared__ float smem[];
     const int unit = blockIdx.x;
     const int uh = unit / P.S;
@@ -79,7 +79,7 @@ hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_i
     const int64_t nblocks = (int64_t)rows.R * kv.Hkv * num_splits;
     const int blocks_per_wg = num_splits > 1 && blocked ? (k + num_splits - 1) / num_splits : k;
     P.table_words = 4 * ((blocks_per_wg + 3) & ~3);  // keeps the K tiles 16-byte aligned
-    const size_t loop = (size_t)P.table_words * 4 + attn_tile_bytes(kv.kv_fp8 != 0);
+    const size_t loop = attn_loop_bytes(P.table_words, kv.kv_fp8 != 0);
     const size_t xchg = (size_t)kAttnWaves * P.g * kHeadDim * sizeof(float);
     const size_t lds = loop > xchg ? loop : xchg;
     if (kv.kv_fp8)

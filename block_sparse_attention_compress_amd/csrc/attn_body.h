@@ -20,6 +20,16 @@ constexpr int kTileRowBytes = KV8 ? kKRow8 : 2 * kKRow;
 __host__ __device__ constexpr size_t attn_tile_bytes(bool kv8) {
     return (size_t)kAttnWaves * 2 * 16 * (kv8 ? kTileRowBytes<true> : kTileRowBytes<false>);
 }
+// An fp8 cache's kernel keeps the query operand in LDS (16 padded bf16 rows after
+// the tiles) rather than in 32 registers, which fits it in 168 registers: 3 waves
+// per SIMD, and 3 workgroups per CU within the LDS.  A bf16 cache's loop is bound
+// by its L2 gathers, not by latency, and keeps the query in registers.
+constexpr int kQRow = kHeadDim + 8;  // padded query row in LDS (elements)
+__host__ __device__ constexpr size_t attn_q_bytes(bool kv8) { return kv8 ? (size_t)16 * kQRow * 2 : 0; }
+// LDS bytes of the loop: slot table, staging tiles, query rows (fp8 cache)
+__host__ __device__ constexpr size_t attn_loop_bytes(int table_words, bool kv8) {
+    return (size_t)table_words * 4 + attn_tile_bytes(kv8) + attn_q_bytes(kv8);
+}
 
 typedef short bf16x4s __attribute__((ext_vector_type(4)));
 
@@ -104,7 +114,18 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
     // together.  Blocked splits cut the k selection slots (not the count), so the
     // selection reads need not wait for the count.
     bf16x8 qb[8];
-    {
+    uint16_t* qlds = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(smem + P.table_words) + attn_tile_bytes(KV8));
+    if constexpr (KV8) {
+        // 16 rows of 256 dims (rows g..15 zero), 16 bytes per thread and pass;
+        // read back by the loop after the slot table's barrier
+        const uint16_t* qp = P.q + (int64_t)row * P.q_stride + (int64_t)h * g * kHeadDim;
+#pragma unroll
+        for (int e = tid; e < 16 * (kHeadDim / 8); e += 256) {
+            const int hh = e / (kHeadDim / 8), d = 8 * (e % (kHeadDim / 8));
+            const bf16x8 x = hh < g ? *reinterpret_cast<const bf16x8*>(qp + hh * kHeadDim + d) : bf16x8{};
+            *reinterpret_cast<bf16x8*>(qlds + hh * kQRow + d) = x;
+        }
+    } else {
         const uint16_t* qp = P.q + (int64_t)row * P.q_stride + (int64_t)(h * g + min(c, g - 1)) * kHeadDim + 8 * qq;
 #pragma unroll
         for (int m = 0; m < 8; ++m) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 32 * m);
@@ -189,7 +210,10 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
 #pragma unroll
             for (int m = 0; m < 8; ++m) kb[m] = k_operand(m);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[m], qb[m], st, 0, 0, 0);
+            for (int m = 0; m < 8; ++m) {
+                const bf16x8 qm = KV8 ? *reinterpret_cast<const bf16x8*>(qlds + c * kQRow + 32 * m + 8 * qq) : qb[m];
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[m], qm, st, 0, 0, 0);
+            }
         }
         uint4 vv[4][2];
 #pragma unroll
@@ -225,10 +249,9 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         float psum = 0.f;
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-            const uint32_t lo = f32_to_bf16_rne(__builtin_amdgcn_exp2f(x[2 * w] - m_use));
-            const uint32_t hi = f32_to_bf16_rne(__builtin_amdgcn_exp2f(x[2 * w + 1] - m_use));
-            psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
-            pw[w] = lo | (hi << 16);
+            pw[w] = pack_bf16x2_hw(__builtin_amdgcn_exp2f(x[2 * w] - m_use),
+                                   __builtin_amdgcn_exp2f(x[2 * w + 1] - m_use));
+            psum += bf16_lo(pw[w]) + bf16_hi(pw[w]);
         }
         l_run += psum;
         // ---- zero the V of masked slots (their weight is 0, their bytes may be anything)
@@ -413,7 +436,7 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         } else {
             uint16_t* dst = P.out + (int64_t)row * P.out_stride + (int64_t)head * kHeadDim + d;
             if (out8) {
-                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2_hw(o.x, o.y), pack_bf16x2_hw(o.z, o.w));
             } else {
                 dst[0] = (uint16_t)f32_to_bf16_rne(o.x);
                 dst[1] = (uint16_t)f32_to_bf16_rne(o.y);

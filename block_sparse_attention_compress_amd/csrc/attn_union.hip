@@ -306,10 +306,9 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
                     float psum = 0.f;
 #pragma unroll
                     for (int w = 0; w < 2; ++w) {
-                        const uint32_t lo = f32_to_bf16_rne(__builtin_amdgcn_exp2f(x[2 * w] - m_use));
-                        const uint32_t hi = f32_to_bf16_rne(__builtin_amdgcn_exp2f(x[2 * w + 1] - m_use));
-                        psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
-                        pw[w] = lo | (hi << 16);
+                        pw[w] = pack_bf16x2_hw(__builtin_amdgcn_exp2f(x[2 * w] - m_use),
+                                               __builtin_amdgcn_exp2f(x[2 * w + 1] - m_use));
+                        psum += bf16_lo(pw[w]) + bf16_hi(pw[w]);
                     }
                     l_run += psum;
 #pragma unroll
@@ -375,7 +374,7 @@ __global__ __launch_bounds__(kUThreads) void attn_union_kernel(const UnionParams
             const int d = 128 * hf + 8 * c;
             uint32_t w[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(O[8 * hf + 2 * j][i] * inv, O[8 * hf + 2 * j + 1][i] * inv);
+            for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2_hw(O[8 * hf + 2 * j][i] * inv, O[8 * hf + 2 * j + 1][i] * inv);
             uint16_t* p = dst + d;
             if (((reinterpret_cast<uintptr_t>(p)) & 15) == 0) {
                 *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);

@@ -733,7 +733,7 @@ hipError_t launch_fused_decode(const PagedKV& kv, const Rows& rows, int k, float
         if (v >= 1 && v < kSpinLimit) F.spin_limit = (int)v;
     }
 
-    const size_t attn_loop = (size_t)A.table_words * 4 + attn_tile_bytes(kv.kv_fp8 != 0);
+    const size_t attn_loop = attn_loop_bytes(A.table_words, kv.kv_fp8 != 0);
     const size_t attn_xchg = (size_t)kAttnWaves * A.g * kHeadDim * sizeof(float);
     size_t lds = attn_loop > attn_xchg ? attn_loop : attn_xchg;
     if (lds < (size_t)kSelLdsInts * 4) lds = (size_t)kSelLdsInts * 4;

@@ -26,6 +26,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// The same packing by the hardware conversion (one v_cvt_pk_bf16_f32, round to
+// nearest even): equal to pack_bf16x2 for finite inputs.  Used where the
+// rounding sits in a hot loop (attention weights, outputs); block keys keep the
+// integer form above.
+typedef float qsa_f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 qsa_bf2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((qsa_f2v){lo, hi}, qsa_bf2v));
+}
+
 // Streaming loads: the nontemporal hint keeps data read once (the block-key
 // scan) from being allocated in the caches on its way through.
 typedef float qsa_f4v __attribute__((ext_vector_type(4)));
@@ -109,5 +119,16 @@ __device__ __forceinline__ int wave_max_int(int v) {
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// MI355X hands a launch's workgroups to its 8 XCDs in turn (linear workgroup b to
+// XCD b mod 8), and each XCD has its own L2.  xcd_unit(b, n) renumbers the n
+// workgroups so that XCD x takes a contiguous range of units in order: units
+// that read the same rows (neighbouring extend rows, row tiles over one key
+// chunk) then meet in one L2 instead of being fetched into eight.  A bijection
+// of [0, n) for every n.
+__device__ __forceinline__ int xcd_unit(int b, int n) {
+    const int x = b & 7;
+    return x * (n >> 3) + min(x, n & 7) + (b >> 3);
+}
 
 }  // namespace qsa
