@@ -120,15 +120,4 @@ __device__ __forceinline__ int wave_max_int(int v) {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// MI355X hands a launch's workgroups to its 8 XCDs in turn (linear workgroup b to
-// XCD b mod 8), and each XCD has its own L2.  xcd_unit(b, n) renumbers the n
-// workgroups so that XCD x takes a contiguous range of units in order: units
-// that read the same rows (neighbouring extend rows, row tiles over one key
-// chunk) then meet in one L2 instead of being fetched into eight.  A bijection
-// of [0, n) for every n.
-__device__ __forceinline__ int xcd_unit(int b, int n) {
-    const int x = b & 7;
-    return x * (n >> 3) + min(x, n & 7) + (b >> 3);
-}
-
 }  // namespace qsa

@@ -126,19 +126,12 @@ __global__ __launch_bounds__(64 * NW) void scores_tiled_kernel(
     constexpr int FPT = 64 / TPB;      // float4 (Raw) pieces per thread
     typedef typename KeyRaw<KT>::type Raw;
     const Raw* keys = reinterpret_cast<const Raw*>(ckey);  // a block key is 64 Raw
-    // fp32 keys: workgroups numbered by XCD, so the row tiles of one key chunk meet
-    // in one L2 (the C4 chunk's scores 158-161 -> 150-154 us, the 7,810-row
-    // prefill's 1.12 -> 1.08 ms).  bf16 keys measured slower that way (86 -> 92 us
-    // at C4) and keep the dispatch order.
-    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int wg = KT == kKeyF32 ? xcd_unit(lin, gridDim.x * gridDim.y * gridDim.z) : lin;
-    const int bx = wg % gridDim.x;
-    const int h = (wg / gridDim.x) % gridDim.y;
-    const int bc0 = (wg / (gridDim.x * gridDim.y)) * kTiledChunk;  // this workgroup's first block
+    const int h = blockIdx.y;
+    const int bc0 = blockIdx.z * kTiledChunk;  // this workgroup's first block
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = wave_id();
-    const int r0 = bx * (16 * NW) + wave * 16;
+    const int r0 = blockIdx.x * (16 * NW) + wave * 16;
     const int c = lane & 15, kq = lane >> 4;
     const int row = r0 + c;
     const bool valid = row < R;
