@@ -78,7 +78,7 @@ hipError_t launch_attn(const PagedKV& kv, const Rows& rows, const int32_t* sel_i
     P.part_lse = o.part_lse;
     const int64_t nblocks = (int64_t)rows.R * kv.Hkv * num_splits;
     const int blocks_per_wg = num_splits > 1 && blocked ? (k + num_splits - 1) / num_splits : k;
-    P.table_words = 4 * ((blocks_per_wg + 3) & ~3);  // keeps the K tiles 16-byte aligned
+    P.table_words = 4 * ((blocks_per_wg + 3) & ~3) + kSlotPad;  // keeps the K tiles 16-byte aligned
     const size_t loop = attn_loop_bytes(P.table_words, kv.kv_fp8 != 0);
     const size_t xchg = (size_t)kAttnWaves * P.g * kHeadDim * sizeof(float);
     const size_t lds = loop > xchg ? loop : xchg;

@@ -9,6 +9,10 @@
 namespace qsa {
 
 constexpr int kAttnWaves = 4;
+// Slot-table entries past a work unit's last token, all -1: the tile pipeline
+// reads the slots of each wave's next tile unclamped, up to 16 kAttnWaves + 15
+// past the last one.
+constexpr int kSlotPad = 16 * kAttnWaves + 16;
 constexpr int kMaxSel = 2048;
 constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
 constexpr int kKRow = kHeadDim + 8;   // padded K row in the LDS tile (elements): spreads rows over banks
@@ -88,7 +92,8 @@ __device__ __forceinline__ uint4 kv_bf16x8(const uint2& x) {
 }
 
 // LDS: `smem` is dynamic shared memory of the launch: the slot table (16 B per
-// selected block of this work unit, P.table_words int32) and the 4 waves' K and V
+// selected block of this work unit and kSlotPad entries of -1, P.table_words
+// int32) and the 4 waves' K and V
 // staging tiles, later reused for the waves' O exchange (4 waves x g heads x
 // 1 KiB); the launch sizes it to the larger need.  Ends with a barrier-free
 // write of the result; the caller separates work units sharing `smem` with a
@@ -167,6 +172,7 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         *reinterpret_cast<int4*>(slot_row + 4 * (j - jb)) = make_int4(
             nv > 0 ? base : -1, nv > 1 ? base + 1 : -1, nv > 2 ? base + 2 : -1, nv > 3 ? base + 3 : -1);
     }
+    for (int i = tid; i < kSlotPad; i += 256) slot_row[4 * (je - jb) + i] = -1;
     __syncthreads();
 
     // split-local slot n lives at table entry slot0 + sstep * n
@@ -293,26 +299,54 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
     // (the raw tile is 16 named registers, not an array: an array indexed in a
     // loop across the tile pipeline was kept in scratch memory)
     Raw k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
-    // The slot reads are unconditional (index clamped to the last slot, result
-    // masked after), so that the 12 LDS reads of a tile issue back to back rather
-    // than one round trip per load, and the next tile's are issued before this
-    // tile's staging writes.  Slot 0 exists in the table, or in the tiles after
-    // it, even when n_s is 0.
+    // The slot reads are unconditional, so that a tile's LDS reads issue back to
+    // back rather than one round trip per load, and the next tile's are issued
+    // before this tile's staging writes.  The index is clamped to the last slot,
+    // and a slot past the split's end loads row 0 (bf16 rows: one cached line);
+    // `live` masks those tokens (their weight and V slice are zeroed).
+    // fp8 rows, whose loop is bound by its vector-ALU work and its loads in flight
+    // rather than by the gathers, use a leaner form (C4 extend attention 385 ->
+    // 353 us; with bf16 rows the same form measured 2-3 % slower): with a slot
+    // step of 1 (the split's slots are consecutive table entries from 0) the
+    // table is read directly -- the kSlotPad entries after the last slot are -1 --
+    // from two addresses with immediate offsets, and no load tests its slot
+    // against the split's end: a slot past it reads -1 or the last slot's cache
+    // row, both inside the cache (-1 reads row 0).  With no slot at all
+    // (n_s == 0) nothing is loaded.
     const int last_slot = max(n_s - 1, 0);
+    // this lane's bytes of a row, folded into the K and V bases (fp8 rows)
+    const uint8_t* kb_lane = reinterpret_cast<const uint8_t*>(P.k) + sizeof(Raw) * (lane & 31);
+    const uint8_t* vb_lane = reinterpret_cast<const uint8_t*>(P.v) + sizeof(Raw) * (lane & 31);
     int n0_, rr_[8], lv_[4];
 #define QSA_SLOT(N) slot_row[slot0 + sstep * min((N), last_slot)]
-#define QSA_SLOTS(TILE)                                                                     \
+#define QSA_SLOTS(TILE, DIRECT)                                                             \
     do {                                                                                    \
         n0_ = (TILE) * 16;                                                                  \
-        _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rr_[j_] = QSA_SLOT(n0_ + 2 * j_ + (lane >> 5)); \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) lv_[i_] = QSA_SLOT(n0_ + 4 * qq + i_); \
+        if constexpr (DIRECT) {                                                             \
+            const int32_t* sr_ = slot_row + n0_ + (lane >> 5);                              \
+            _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rr_[j_] = sr_[2 * j_];         \
+            const int4 l4_ = *reinterpret_cast<const int4*>(slot_row + n0_ + 4 * qq);      \
+            lv_[0] = l4_.x;                                                                 \
+            lv_[1] = l4_.y;                                                                 \
+            lv_[2] = l4_.z;                                                                 \
+            lv_[3] = l4_.w;                                                                 \
+        } else {                                                                            \
+            _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rr_[j_] = QSA_SLOT(n0_ + 2 * j_ + (lane >> 5)); \
+            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) lv_[i_] = QSA_SLOT(n0_ + 4 * qq + i_); \
+        }                                                                                   \
     } while (0)
 #define QSA_LOAD_J(J, KX, VX)                                                               \
     do {                                                                                    \
-        const int rr = n0_ + 2 * (J) + (lane >> 5) < n_s ? rr_[J] : -1;                     \
-        const int64_t off = (int64_t)max(rr, 0) * kHeadDim * EB + sizeof(Raw) * (lane & 31); \
-        KX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.k) + off);    \
-        VX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.v) + off);    \
+        if constexpr (KV8) {                                                                \
+            const int64_t off = (int64_t)max(rr_[J], 0) * (kHeadDim * EB);                  \
+            KX = *reinterpret_cast<const Raw*>(kb_lane + off);                              \
+            VX = *reinterpret_cast<const Raw*>(vb_lane + off);                              \
+        } else {                                                                            \
+            const int rr = n0_ + 2 * (J) + (lane >> 5) < n_s ? rr_[J] : -1;                 \
+            const int64_t off = (int64_t)max(rr, 0) * kHeadDim * EB + sizeof(Raw) * (lane & 31); \
+            KX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.k) + off); \
+            VX = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(P.v) + off); \
+        }                                                                                   \
     } while (0)
 #define QSA_LOAD_RAW(LIVE)                                                                  \
     do {                                                                                    \
@@ -335,26 +369,39 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
         *reinterpret_cast<Raw*>(ktile + r * RB + sizeof(Raw) * (lane & 31)) = KX;           \
         *reinterpret_cast<Raw*>(vtile + r * RB + sizeof(Raw) * (lane & 31)) = VX;           \
     } while (0)
-    // past the last tile every slot reads as masked: the loads then all hit row 0
-    // (one cached line) and no branch breaks the register pipeline; a masked row
-    // holds row 0's bytes, whose weight and V slice are zeroed
+// The tile pipeline.  DIRECT: the split's slots are table entries 0, 1, 2, ...
+// (slot step 1), read without a clamp (fp8 rows).
+#define QSA_TILE_LOOP(DIRECT)                                                               \
+    do {                                                                                    \
+        if (!KV8 || n_s > 0) { /* bf16 rows test each load's slot against n_s */           \
+            QSA_SLOTS(wave, DIRECT);                                                        \
+            QSA_LOAD_RAW(live_next);                                                        \
+        }                                                                                   \
+        for (int tile = wave; tile < ntiles; tile += kAttnWaves) {                          \
+            QSA_SLOTS(tile + kAttnWaves, DIRECT);                                           \
+            QSA_STAGE_J(0, k0, v0);                                                         \
+            QSA_STAGE_J(1, k1, v1);                                                         \
+            QSA_STAGE_J(2, k2, v2);                                                         \
+            QSA_STAGE_J(3, k3, v3);                                                         \
+            QSA_STAGE_J(4, k4, v4);                                                         \
+            QSA_STAGE_J(5, k5, v5);                                                         \
+            QSA_STAGE_J(6, k6, v6);                                                         \
+            QSA_STAGE_J(7, k7, v7);                                                         \
+            const int live = live_next;                                                     \
+            QSA_LOAD_RAW(live_next);                                                        \
+            compute_tile(live);                                                             \
+        }                                                                                   \
+    } while (0)
     int live_next;
-    QSA_SLOTS(wave);
-    QSA_LOAD_RAW(live_next);
-    for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
-        QSA_SLOTS(tile + kAttnWaves);
-        QSA_STAGE_J(0, k0, v0);
-        QSA_STAGE_J(1, k1, v1);
-        QSA_STAGE_J(2, k2, v2);
-        QSA_STAGE_J(3, k3, v3);
-        QSA_STAGE_J(4, k4, v4);
-        QSA_STAGE_J(5, k5, v5);
-        QSA_STAGE_J(6, k6, v6);
-        QSA_STAGE_J(7, k7, v7);
-        const int live = live_next;
-        QSA_LOAD_RAW(live_next);
-        compute_tile(live);
+    if constexpr (KV8) {
+        if (sstep == 1)
+            QSA_TILE_LOOP(true);
+        else
+            QSA_TILE_LOOP(false);
+    } else {
+        QSA_TILE_LOOP(false);
     }
+#undef QSA_TILE_LOOP
 #undef QSA_LOAD_RAW
 #undef QSA_LOAD_J
 #undef QSA_SLOT

@@ -696,7 +696,7 @@ hipError_t launch_fused_decode(const PagedKV& kv, const Rows& rows, int k, float
     A.S = S;
     A.blocked = 1;
     const int blocks_per_split = (k + S - 1) / S;
-    A.table_words = 4 * ((blocks_per_split + 3) & ~3);
+    A.table_words = 4 * ((blocks_per_split + 3) & ~3) + kSlotPad;
     A.out = nullptr;
     A.out_stride = 0;
     A.lse = nullptr;
