@@ -275,22 +275,26 @@ def test_selection_widths(L, k):
     check_decode_against_oracle(case, *res, k)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("num_splits", [0, 1, 5])
-def test_largest_k(num_splits):
+def test_largest_k(num_splits, kv_dtype):
     """k = 2048, the most allowed: 8,192 selected tokens per (row, KV head), the
-    largest slot table and token loop, with the library's splits, one split and 5;
-    a 300-token row selects all of its 75 blocks."""
-    case = small_decode(f"k2048s{num_splits}", 88 + num_splits, 16, 2, [10000, 9001, 300], 64, topk=2048,
-                        jitter=True)
-    log(f"k=2048 splits={num_splits}")
+    largest slot table and token loop, with the library's splits, one split and 5,
+    for both cache types; a 300-token row selects all of its 75 blocks."""
+    case = small_decode(f"k2048s{num_splits}{kv_dtype}", 88 + num_splits, 16, 2, [10000, 9001, 300], 64, topk=2048,
+                        jitter=True, kv_dtype=kv_dtype)
+    log(f"k=2048 splits={num_splits} cache={kv_dtype}")
     res = run_decode(case, k=2048, num_splits=num_splits)
     check_decode_against_oracle(case, *res, 2048)
 
 
-def test_largest_k_extend():
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_largest_k_extend(kv_dtype):
     total, nq = 12000, 65
     q_seq, q_pos = synth.extend_rows(total, nq)
-    case = synth.make_case("k2048ext", 89, 12, 1, [total], page_size=64, q_seq=q_seq, q_pos=q_pos, topk=2048)
+    case = synth.make_case(f"k2048ext{kv_dtype}", 89, 12, 1, [total], page_size=64, q_seq=q_seq, q_pos=q_pos,
+                           topk=2048, kv_dtype=kv_dtype)
+    log(f"extend k=2048 cache={kv_dtype}")
     res = run_extend(case, k=2048)
     check_decode_against_oracle(case, *res, 2048)
 
