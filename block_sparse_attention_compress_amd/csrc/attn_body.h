@@ -305,8 +305,8 @@ __device__ __forceinline__ void attend_split(const AttnParams& P, int row, int h
     // and a slot past the split's end loads row 0 (bf16 rows: one cached line);
     // `live` masks those tokens (their weight and V slice are zeroed).
     // fp8 rows, whose loop is bound by its vector-ALU work and its loads in flight
-    // rather than by the gathers, use a leaner form (C4 extend attention 385 ->
-    // 353 us; with bf16 rows the same form measured 2-3 % slower): with a slot
+    // rather than by the gathers, use a leaner form (C4 extend attention 380-431
+    // -> 360-368 us; with bf16 rows the same form measured 2-3 % slower): with a slot
     // step of 1 (the split's slots are consecutive table entries from 0) the
     // table is read directly -- the kSlotPad entries after the last slot are -1 --
     // from two addresses with immediate offsets, and no load tests its slot
