@@ -17,8 +17,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libqsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["qsa_api.hip", "compress.hip", "scores.hip", "topk.hip", "attn.hip", "attn_union.hip", "merge.hip",
-           "fused.hip"]
+SOURCES = ["qsa_api.hip", "compress.hip", "scores.hip", "scores_tiled.hip", "topk.hip", "attn.hip",
+           "attn_union.hip", "merge.hip", "fused.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950",
