@@ -570,6 +570,67 @@ def extend_figures(steps: int, flush: bool = False, ckey_dtype: str = "fp32", kv
             "cpu_baseline": extend_cpu_baseline(case, cpu_seconds) if cpu_seconds > 0 else None}
 
 
+def small_chunk_figures(steps: int, kv_dtype: str = "bf16", ckey_dtype: str = "fp32", rows=(32, 64, 128)):
+    """Extend chunks of few rows: the newest R tokens of one 32,768-token sequence, (12,1)
+    heads, top-512.  The chunk's attention with one workgroup per (row, KV head) against
+    the split read merged by log-sum-exp (qsa_sparse_attn_extend_split, the library's split
+    count), and the whole chunk (block keys of the new tokens, scores, top-k, attention)
+    both ways."""
+    import torch
+
+    import block_sparse_attention_compress_amd as qsa
+    import synth
+    from block_sparse_attention_compress_amd.pipeline import ExtendBuffers, extend_step
+
+    def wall(fn, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / n * 1e3
+
+    total = 32768
+    out = []
+    for R in rows:
+        q_pos = list(range(total - R, total))
+        case = synth.make_case(f"small{R}", 700 + R, 12, 1, [total], page_size=total, q_seq=[0] * R, q_pos=q_pos,
+                               shuffle=False, ckey_dtype=ckey_dtype, kv_dtype=kv_dtype)
+        dev = synth.to_device(case, "cuda")
+        kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
+        qsa.qsa_compress_keys(kv)
+        first = torch.tensor([total - R], dtype=torch.int32, device="cuda")
+        stride = case.nb(0)
+        buf = ExtendBuffers.allocate(R, case.Hq, case.Hkv, stride, 512, "cuda", max_splits=0)
+        q, q_seq, qp = dev["q"], dev["q_seq"], dev["q_pos"]
+        ws = buf.workspace
+        wsb = ws.numel() if ws is not None else 0
+        attn = {
+            "unsplit": lambda: qsa.qsa_sparse_attn_extend(kv, q, q.stride(0), q_seq, qp, R, case.Hq, buf.sel_idx,
+                                                          buf.sel_cnt, 512, case.scale, buf.out, buf.out.stride(0),
+                                                          buf.lse),
+            "split": lambda: qsa.qsa_sparse_attn_extend_split(kv, q, q.stride(0), q_seq, qp, R, case.Hq, buf.sel_idx,
+                                                              buf.sel_cnt, 512, case.scale, 0, buf.out,
+                                                              buf.out.stride(0), buf.lse, workspace=ws,
+                                                              workspace_bytes=wsb),
+        }
+        extend_step(kv, q, q_seq, qp, buf, first, scale=case.scale)
+        torch.cuda.synchronize()
+        rec = {"new_tokens": R, "context": total}
+        for name, f in attn.items():
+            f()
+            rec[f"attention_ms_{name}"] = round(wall(f, steps), 5)
+        for name, S in (("unsplit", 1), ("split", 0)):
+            step = lambda: extend_step(kv, q, q_seq, qp, buf, first, scale=case.scale, num_splits=S)
+            step()
+            rec[f"chunk_ms_{name}"] = round(wall(step, steps), 5)
+        log(f"small extend chunk {R} rows: attention {rec['attention_ms_unsplit']} -> {rec['attention_ms_split']} ms, "
+            f"chunk {rec['chunk_ms_unsplit']} -> {rec['chunk_ms_split']} ms")
+        out.append(rec)
+        del dev, kv, buf
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -619,6 +680,7 @@ def main():
     if not args.no_extend:
         result["extend"] = extend_figures(max(20, args.steps // 2), args.flush, args.ckey, args.kv,
                                           cpu_seconds=0.0 if args.no_cpu_baseline else 0.4 * args.cpu_seconds)
+        result["extend"]["small_chunks"] = small_chunk_figures(max(20, args.steps // 2), args.kv, args.ckey)
     print(json.dumps(result), flush=True)
 
 

@@ -44,7 +44,7 @@ EXPORTS = ("qsa_version", "qsa_last_error", "qsa_compress_keys", "qsa_block_scor
            "qsa_sparse_attn_decode", "qsa_decode_workspace_bytes", "qsa_sparse_attn_extend", "qsa_merge_lse",
            "qsa_decode_fused", "qsa_decode_fused_workspace_bytes", "qsa_topk_blocks_ws",
            "qsa_topk_workspace_bytes", "qsa_decode_scores_refresh", "qsa_sparse_attn_decode_noalloc",
-           "qsa_sparse_attn_extend_union")
+           "qsa_sparse_attn_extend_union", "qsa_sparse_attn_extend_split", "qsa_extend_workspace_bytes")
 
 
 class QsaError(RuntimeError):
@@ -98,13 +98,17 @@ def lib() -> ctypes.CDLL:
         L.qsa_sparse_attn_decode_noalloc.argtypes = [kvp, vp, i64, i32, vp, vp, i32, f32, i32, vp, i64, vp, vp]
         L.qsa_sparse_attn_extend.argtypes = [kvp, vp, i64, vp, vp, i32, i32, vp, vp, i32, f32, vp, i64, vp, vp]
         L.qsa_sparse_attn_extend_union.argtypes = [kvp, vp, i64, vp, vp, i32, i32, vp, vp, i32, f32, vp, i64, vp, vp]
+        L.qsa_sparse_attn_extend_split.argtypes = [kvp, vp, i64, vp, vp, i32, i32, vp, vp, i32, f32, i32, vp, i64, vp,
+                                                   vp, sz, vp]
+        L.qsa_extend_workspace_bytes.argtypes, L.qsa_extend_workspace_bytes.restype = [i32, i32, i32], sz
         L.qsa_merge_lse.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.qsa_decode_fused.argtypes = [kvp, vp, i64, i32, i32, f32, i32, vp, vp, vp, i64, vp, vp, sz, vp]
         L.qsa_decode_fused_workspace_bytes.argtypes = [kvp, i32, i32, i32]
         L.qsa_decode_fused_workspace_bytes.restype = sz
         for f in ("qsa_compress_keys", "qsa_block_scores", "qsa_decode_scores_refresh", "qsa_topk_blocks",
                   "qsa_topk_blocks_ws", "qsa_sparse_attn_decode", "qsa_sparse_attn_extend", "qsa_merge_lse",
-                  "qsa_decode_fused", "qsa_sparse_attn_decode_noalloc", "qsa_sparse_attn_extend_union"):
+                  "qsa_decode_fused", "qsa_sparse_attn_decode_noalloc", "qsa_sparse_attn_extend_union",
+                  "qsa_sparse_attn_extend_split"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -230,6 +234,20 @@ def qsa_sparse_attn_extend(kv, q, q_row_stride: int, q_seq, q_pos, R: int, Hq: i
     _check(lib().qsa_sparse_attn_extend(ctypes.byref(d), _ptr(q), q_row_stride, _ptr(q_seq), _ptr(q_pos), R, Hq,
                                         _ptr(sel_idx), _ptr(sel_cnt), k, scale, _ptr(out), out_row_stride,
                                         _ptr(lse), _stream(stream)))
+
+
+def qsa_extend_workspace_bytes(R: int, Hq: int, num_splits: int) -> int:
+    return int(lib().qsa_extend_workspace_bytes(R, Hq, num_splits))
+
+
+def qsa_sparse_attn_extend_split(kv, q, q_row_stride: int, q_seq, q_pos, R: int, Hq: int, sel_idx, sel_cnt, k: int,
+                                 scale: float, num_splits: int, out, out_row_stride: int, lse=None, workspace=None,
+                                 workspace_bytes: int = 0, stream=None) -> None:
+    d = _kv(kv)
+    _check(lib().qsa_sparse_attn_extend_split(ctypes.byref(d), _ptr(q), q_row_stride, _ptr(q_seq), _ptr(q_pos), R, Hq,
+                                              _ptr(sel_idx), _ptr(sel_cnt), k, scale, num_splits, _ptr(out),
+                                              out_row_stride, _ptr(lse), _ptr(workspace), workspace_bytes,
+                                              _stream(stream)))
 
 
 def qsa_sparse_attn_extend_union(kv, q, q_row_stride: int, q_seq, q_pos, R: int, Hq: int, sel_idx, sel_cnt, k: int,

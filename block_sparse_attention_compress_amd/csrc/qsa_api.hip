@@ -149,44 +149,46 @@ int scratch_for_current_device(void** ptr) {
     return QSA_OK;
 }
 
-// Decode attention writing the final result (out, lse): one launch when the split
-// count is 1, else blocked split partials and the merge.  The partials go to the
-// caller's `workspace`, or with use_scratch to the static scratch (the
-// no-allocation entry point; workspace is then ignored).
-int decode_final(const qsa::PagedKV& p, const qsa::Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt,
+// Attention writing the final result (out, lse) of rows.R rows (decode: one per
+// sequence; extend: rows.q_seq / rows.q_pos): one launch when the split count is
+// 1, else blocked split partials and the merge.  The partials go to the caller's
+// `workspace`, or with use_scratch to the static scratch (the no-allocation
+// entry point; workspace is then ignored).
+int attn_final(const qsa::PagedKV& p, const qsa::Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt,
                  int32_t k, float sc, int32_t num_splits, void* out, int64_t out_row_stride, float* lse,
                  void* workspace, size_t workspace_bytes, bool use_scratch, hipStream_t st, const char* what) {
     const int Hq = rows.Hq;
     if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
     if (out_row_stride < (int64_t)Hq * QSA_HEAD_DIM)
         return fail(QSA_ERR_INVALID_ARG, "out_row_stride %lld < Hq * 256", (long long)out_row_stride);
-    const int S = num_splits == 0 ? auto_splits((int64_t)p.batch * p.Hkv, k) : num_splits;
+    const int R = rows.R;
+    const int S = num_splits == 0 ? auto_splits((int64_t)R * p.Hkv, k) : num_splits;
     if (S == 1) {
         qsa::AttnOut o{static_cast<uint16_t*>(out), out_row_stride, lse, nullptr, nullptr};
         return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, false, o, st), what);
     }
     if (out_row_stride != (int64_t)Hq * QSA_HEAD_DIM || !aligned(out, 8))
-        return fail(QSA_ERR_UNSUPPORTED, "a split decode writes a dense, 8-byte aligned out");
-    const size_t need = qsa_decode_workspace_bytes(p.batch, Hq, S);
+        return fail(QSA_ERR_UNSUPPORTED, "a split attention writes a dense, 8-byte aligned out");
+    const size_t need = qsa_decode_workspace_bytes(R, Hq, S);
     if (use_scratch) {
         if (need > kScratchBytes)
             return fail(QSA_ERR_UNSUPPORTED,
                         "%d splits of %d rows x %d heads need %zu bytes of partials, more than the %zu bytes of "
                         "static scratch (use qsa_sparse_attn_decode with a workspace, or fewer splits)",
-                        S, p.batch, Hq, need, (size_t)kScratchBytes);
+                        S, R, Hq, need, (size_t)kScratchBytes);
         if (int rc = scratch_for_current_device(&workspace)) return rc;
         workspace_bytes = kScratchBytes;
     } else if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) {
         return fail(QSA_ERR_INVALID_ARG, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);
     }
-    const int64_t n = (int64_t)S * p.batch * Hq;
+    const int64_t n = (int64_t)S * R * Hq;
     float* wo = static_cast<float*>(workspace);
     float* wl = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          (((size_t)n * QSA_HEAD_DIM * sizeof(float) + 255) & ~(size_t)255));
     qsa::AttnOut o{nullptr, 0, nullptr, wo, wl};
     if (int rc = hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, S, true, o, st), what)) return rc;
-    return hip_status(qsa::launch_merge(wo, wl, S, p.batch * Hq, QSA_HEAD_DIM, static_cast<uint16_t*>(out), lse, st),
+    return hip_status(qsa::launch_merge(wo, wl, S, R * Hq, QSA_HEAD_DIM, static_cast<uint16_t*>(out), lse, st),
                       what);
 }
 
@@ -326,7 +328,7 @@ int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
         return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, num_splits, false, o, st),
                           "qsa_sparse_attn_decode");
     }
-    return decode_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, workspace,
+    return attn_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, workspace,
                         workspace_bytes, false, st, "qsa_sparse_attn_decode");
 }
 
@@ -345,7 +347,7 @@ int qsa_sparse_attn_decode_noalloc(const qsa_kv_t* kv, const void* q, int64_t q_
         return fail(QSA_ERR_UNSUPPORTED, "too many work units");
     const float sc = scale > 0.f ? scale : 0.0625f;
     qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, nullptr, nullptr, p.batch, Hq};
-    return decode_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, nullptr, 0, true,
+    return attn_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, nullptr, 0, true,
                         static_cast<hipStream_t>(stream), "qsa_sparse_attn_decode_noalloc");
 }
 
@@ -408,6 +410,36 @@ int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
     qsa::AttnOut o{static_cast<uint16_t*>(out), out_row_stride, lse, nullptr, nullptr};
     return hip_status(qsa::launch_attn(p, rows, sel_idx, sel_cnt, k, sc, 1, false, o, static_cast<hipStream_t>(stream)),
                       "qsa_sparse_attn_extend");
+}
+
+size_t qsa_extend_workspace_bytes(int32_t R, int32_t Hq, int32_t num_splits) {
+    if (num_splits < 0 || num_splits > QSA_MAX_SPLITS) return 0;
+    return qsa_decode_workspace_bytes(R, Hq, num_splits);
+}
+
+int qsa_sparse_attn_extend_split(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,
+                                 const int32_t* q_pos, int32_t R, int32_t Hq, const int32_t* sel_idx,
+                                 const int32_t* sel_cnt, int32_t k, float scale, int32_t num_splits, void* out,
+                                 int64_t out_row_stride, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    qsa::PagedKV p;
+    if (int rc = check_kv(kv, true, true, false, &p)) return rc;
+    if (int rc = check_heads(Hq, p.Hkv)) return rc;
+    if (int rc = check_q(q, q_row_stride, Hq)) return rc;
+    if (!q_seq || !q_pos) return fail(QSA_ERR_INVALID_ARG, "q_seq / q_pos is NULL");
+    if (R < 0) return fail(QSA_ERR_INVALID_ARG, "R %d < 0", R);
+    if (k < 0 || k > QSA_MAX_TOPK) return fail(QSA_ERR_INVALID_ARG, "k %d out of [0, %d]", k, QSA_MAX_TOPK);
+    if (!sel_cnt || (k > 0 && !sel_idx)) return fail(QSA_ERR_INVALID_ARG, "sel_idx / sel_cnt is NULL");
+    if (num_splits < 0 || num_splits > QSA_MAX_SPLITS)
+        return fail(QSA_ERR_INVALID_ARG, "num_splits %d out of [0, %d]", num_splits, QSA_MAX_SPLITS);
+    if ((int64_t)R * p.Hkv * (num_splits > 0 ? num_splits : kAutoSplitMax) > 0x7fffffff)
+        return fail(QSA_ERR_UNSUPPORTED, "too many work units");
+    if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
+    const float sc = scale > 0.f ? scale : 0.0625f;
+    qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, q_seq, q_pos, R, Hq};
+    if (R == 0) return QSA_OK;
+    return attn_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, workspace,
+                      workspace_bytes, false, static_cast<hipStream_t>(stream), "qsa_sparse_attn_extend_split");
 }
 
 int qsa_sparse_attn_extend_union(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, const int32_t* q_seq,

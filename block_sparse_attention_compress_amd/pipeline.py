@@ -13,8 +13,8 @@ import torch
 
 from . import (HEAD_DIM, KVCache, qsa_block_scores, qsa_compress_keys, qsa_decode_fused, qsa_decode_scores_refresh,
                qsa_decode_fused_workspace_bytes, qsa_decode_workspace_bytes, qsa_sparse_attn_decode,
-               qsa_sparse_attn_extend, qsa_sparse_attn_extend_union, qsa_topk_blocks, qsa_topk_blocks_ws,
-               qsa_topk_workspace_bytes)
+               qsa_extend_workspace_bytes, qsa_sparse_attn_extend, qsa_sparse_attn_extend_split,
+               qsa_sparse_attn_extend_union, qsa_topk_blocks, qsa_topk_blocks_ws, qsa_topk_workspace_bytes)
 
 
 @dataclass
@@ -113,30 +113,45 @@ class ExtendBuffers:
     lse: torch.Tensor         # fp32 [R][Hq]
     score_stride: int
     k: int
+    workspace: Optional[torch.Tensor] = None  # split partials of qsa_sparse_attn_extend_split
 
     @staticmethod
-    def allocate(R: int, Hq: int, Hkv: int, score_stride: int, k: int, device="cuda") -> "ExtendBuffers":
+    def allocate(R: int, Hq: int, Hkv: int, score_stride: int, k: int, device="cuda",
+                 max_splits: int = 1) -> "ExtendBuffers":
+        """max_splits: the largest split count the chunk's attention may use (0: any the library chooses)."""
+        ws = qsa_extend_workspace_bytes(R, Hq, max_splits)
         return ExtendBuffers(
             scores=torch.empty((R, Hkv, score_stride), dtype=torch.float32, device=device),
             sel_idx=torch.empty((R, Hkv, max(k, 1)), dtype=torch.int32, device=device),
             sel_cnt=torch.empty((R, Hkv), dtype=torch.int32, device=device),
             out=torch.empty((R, Hq, HEAD_DIM), dtype=torch.bfloat16, device=device),
             lse=torch.empty((R, Hq), dtype=torch.float32, device=device),
-            score_stride=score_stride, k=k)
+            score_stride=score_stride, k=k,
+            workspace=torch.empty(ws, dtype=torch.uint8, device=device) if ws else None)
 
 
 def extend_step(kv: KVCache, q: torch.Tensor, q_seq: torch.Tensor, q_pos: torch.Tensor, buf: ExtendBuffers,
                 first_new: Optional[torch.Tensor] = None, max_new_tokens: int = 0, scale: float = 0.0,
-                stream=None, union_tiles: bool = False) -> None:
+                stream=None, union_tiles: bool = False, num_splits: int = 1) -> None:
     """One extend chunk: block keys of the new tokens (first_new [B] = first new
     position per sequence), then per-row scores, selection and attention (with
-    union_tiles, the query-tile union kernel: the same result sets, usually slower)."""
+    union_tiles, the query-tile union kernel: the same result sets, usually slower;
+    with num_splits != 1, the split read merged by log-sum-exp, for chunks of few
+    rows; 0 lets the library choose the split count)."""
     R, Hq = q.shape[0], q.shape[1]
     Hkv = kv.k.shape[1]
     if first_new is not None:
         qsa_compress_keys(kv, first_new, max_new_tokens, stream=stream)
     qsa_block_scores(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.scores, buf.score_stride, stream=stream)
     qsa_topk_blocks(buf.scores, buf.score_stride, q_pos, R, Hkv, buf.k, buf.sel_idx, buf.sel_cnt, stream=stream)
+    if num_splits != 1:
+        if union_tiles:
+            raise ValueError("the query-tile union kernel has no split read")
+        ws = buf.workspace
+        qsa_sparse_attn_extend_split(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale,
+                                     num_splits, buf.out, buf.out.stride(0), buf.lse, workspace=ws,
+                                     workspace_bytes=ws.numel() if ws is not None else 0, stream=stream)
+        return
     attend = qsa_sparse_attn_extend_union if union_tiles else qsa_sparse_attn_extend
     attend(kv, q, q.stride(0), q_seq, q_pos, R, Hq, buf.sel_idx, buf.sel_cnt, buf.k, scale, buf.out, buf.out.stride(0),
            buf.lse, stream=stream)

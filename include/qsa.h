@@ -322,6 +322,35 @@ QSA_API int qsa_sparse_attn_extend(const qsa_kv_t* kv, const void* q, int64_t q_
                            float* lse, void* stream);
 
 /*
+ * a6 with a split read -- qsa_sparse_attn_extend for chunks of few rows.  Source: the extend rows
+ * of "Qwen4-Exp QSA komt naar Huawei's Ascend", section "Wat de pull request daadwerkelijk
+ * toevoegt", with the split read of "Qwen 4 QSA krijgt decode-contextparallellisme", section "Wat
+ * de pull request daadwerkelijk verandert" (partial attention results over parts of the selected
+ * tokens, combined at the end by log-sum-exp).  Arguments, token sets T and outputs as
+ * qsa_sparse_attn_extend; the selected blocks of each (row, KV head) are cut into S contiguous
+ * ranges, each attended by its own workgroup, and the S partials are merged as qsa_merge_lse does.
+ * The merged result does not depend on the partition, so it equals the unsplit one up to rounding
+ * (fp32 partials, then one bf16 rounding).  num_splits = 0 lets the library choose S from R * Hkv
+ * and k (about 256 workgroups, at least 16 blocks per split, at most 16 splits; 1 once R * Hkv
+ * reaches 256); S = 1 is the unsplit call.  With S > 1, out must be dense (out_row_stride ==
+ * Hq * 256, 8-byte aligned) and `workspace` (device memory owned by the caller, 256-byte aligned)
+ * must hold qsa_extend_workspace_bytes(R, Hq, num_splits) bytes; it holds the partials between
+ * the two launches, so calls sharing it must be ordered on one stream.  Errors: those of
+ * qsa_sparse_attn_extend, QSA_ERR_INVALID_ARG for num_splits outside [0, QSA_MAX_SPLITS] or a
+ * missing, short or misaligned workspace, QSA_ERR_UNSUPPORTED for a strided out with S > 1.
+ */
+QSA_API int qsa_sparse_attn_extend_split(const qsa_kv_t* kv, const void* q, int64_t q_row_stride,
+                                         const int32_t* q_seq, const int32_t* q_pos, int32_t R, int32_t Hq,
+                                         const int32_t* sel_idx, const int32_t* sel_cnt, int32_t k, float scale,
+                                         int32_t num_splits, void* out, int64_t out_row_stride, float* lse,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of qsa_sparse_attn_extend_split: partials for R rows of Hq heads at num_splits
+ * splits (num_splits = 0: enough for any split count the library chooses).  0 when no workspace
+ * is needed (S <= 1) or the arguments are invalid. */
+QSA_API size_t qsa_extend_workspace_bytes(int32_t R, int32_t Hq, int32_t num_splits);
+
+/*
  * a6, query-tile union -- the same attention as qsa_sparse_attn_extend (same arguments, same
  * result set T per row, outputs within rounding of it: only the order in which a row's tokens are
  * summed differs), computed per tile of 8 consecutive query rows and KV head over the union of the

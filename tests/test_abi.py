@@ -220,6 +220,47 @@ def test_extend_and_merge_reject():
     assert m(None, P, 4, 10, 256, P, None, None) == qsa.QSA_ERR_INVALID_ARG
 
 
+def test_extend_split_rejects():
+    d = kv()
+    f = qsa.lib().qsa_sparse_attn_extend_split
+    R, Hq = 10, 16
+    wsb = qsa.qsa_extend_workspace_bytes(R, Hq, 4)
+    assert wsb == qsa.qsa_decode_workspace_bytes(R, Hq, 4) > 0
+    base = [ctypes.byref(d), P, 4096, P, P, R, Hq, P, P, 512, 0.0, 4, P, Hq * 256, None, P, wsb, None]
+    names = ["kv", "q", "qs", "qseq", "qpos", "R", "Hq", "sel", "cnt", "k", "scale", "S", "out", "os", "lse", "ws",
+             "wb", "st"]
+
+    def call(**ch):
+        a = list(base)
+        for n, v in ch.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    assert call(qseq=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(qpos=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(R=-1) == qsa.QSA_ERR_INVALID_ARG
+    assert call(Hq=48, os=48 * 256) == qsa.QSA_ERR_UNSUPPORTED     # g = 24 > 16
+    assert call(k=2049) == qsa.QSA_ERR_INVALID_ARG
+    assert call(cnt=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(S=-1) == qsa.QSA_ERR_INVALID_ARG
+    assert call(S=65) == qsa.QSA_ERR_INVALID_ARG
+    assert call(out=None) == qsa.QSA_ERR_INVALID_ARG
+    assert call(os=100) == qsa.QSA_ERR_INVALID_ARG
+    assert call(ws=None) == qsa.QSA_ERR_INVALID_ARG                 # a split read needs a workspace
+    assert call(wb=wsb - 1) == qsa.QSA_ERR_INVALID_ARG
+    assert call(ws=P + 16) == qsa.QSA_ERR_INVALID_ARG               # 256-byte aligned
+    assert call(os=Hq * 256 + 8) == qsa.QSA_ERR_UNSUPPORTED         # a split read writes dense rows
+    assert call(S=0, ws=None) == qsa.QSA_ERR_INVALID_ARG            # 20 (row, KV head) units: the library splits
+    assert "workspace" in qsa.qsa_last_error()
+    dv = kv(v=None)
+    assert f(ctypes.byref(dv), *base[1:]) == qsa.QSA_ERR_INVALID_ARG
+    # sizes: none for one split or bad arguments; num_splits = 0 covers any split count the library picks
+    assert qsa.qsa_extend_workspace_bytes(R, Hq, 1) == 0
+    assert qsa.qsa_extend_workspace_bytes(R, Hq, 65) == 0
+    assert qsa.qsa_extend_workspace_bytes(0, Hq, 4) == 0
+    assert qsa.qsa_extend_workspace_bytes(R, Hq, 0) == qsa.qsa_extend_workspace_bytes(R, Hq, 16)
+
+
 def test_workspace_size_formula():
     # S partials of [B][Hq][256] fp32 plus [B][Hq] lse, each rounded up to 256 bytes
     S, B, Hq = 4, 3, 6
