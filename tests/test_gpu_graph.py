@@ -1,4 +1,4 @@
-"""A decode step, an extend chunk, and the query-tile union attention, captured in a
+"""A decode step, an extend chunk (also one with the split read), and the query-tile union attention, captured in a
 HIP graph replay to the same bits as the eager calls, on several replays with eager
 work and synchronisations in between."""
 import numpy as np
@@ -98,6 +98,49 @@ def test_extend_chunk_graph_replays_match_eager(kv_dtype):
         graph.replay()
         torch.cuda.synchronize()
         got = (buf.sel_idx, buf.sel_cnt, buf.out, buf.lse, dev["ckey"])
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+        chunk()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_split_extend_chunk_graph_replays_match_eager():
+    """A chunk of few rows with the split read (extend_step(num_splits=0): block keys,
+    tiled scores, top-k, split attention, merge) in one captured graph: every replay
+    bit-equal to the eager chunk, with the workspace poisoned between replays."""
+    total, new = 9000, 40   # 40 (row, KV head) units: the library splits each row 7 ways
+    q_pos = list(range(total - new, total))
+    case = synth.make_case("xsplitgraph", 62, 12, 1, [total], page_size=64, q_seq=[0] * new, q_pos=q_pos,
+                           jitter=True)
+    log("split extend graph replay")
+    dev = synth.to_device(case, "cuda")
+    kv = qsa.KVCache(dev["k"], dev["v"], dev["ckey"], dev["block_table"], dev["seq_lens"], case.max_len)
+    qsa.qsa_compress_keys(kv)
+    first = torch.tensor([total - new], dtype=torch.int32, device="cuda")
+    buf = ExtendBuffers.allocate(case.R, case.Hq, case.Hkv, case.nb(0), case.topk, "cuda", max_splits=0)
+
+    def chunk():
+        extend_step(kv, dev["q"], dev["q_seq"], dev["q_pos"], buf, first, new, scale=case.scale, num_splits=0)
+
+    chunk()
+    torch.cuda.synchronize()
+    want = (buf.sel_idx.clone(), buf.sel_cnt.clone(), buf.out.clone(), buf.lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chunk()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chunk()
+    for rep in range(4):
+        buf.out.fill_(float("nan"))
+        buf.lse.fill_(float("nan"))
+        buf.workspace.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (buf.sel_idx, buf.sel_cnt, buf.out, buf.lse)
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
         chunk()  # eager work between replays
