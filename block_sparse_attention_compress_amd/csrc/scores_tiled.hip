@@ -14,9 +14,15 @@ namespace qsa {
 
 // 16 rows per wave, kTiledWaves waves (64 rows) per workgroup, and `chunk`
 // blocks per workgroup (grid z), so a chunk of new tokens spreads over every CU:
-// kTiledChunk, or fewer (down to 128) when the grid would otherwise hold fewer
-// than 512 workgroups (few rows, or short contexts), where each workgroup's
-// chain of tiles and not the matrix cores sets the time.
+// kTiledChunk, or fewer when the grid would otherwise be small (few rows, or
+// short contexts), where each workgroup's chain of tiles and not the matrix
+// cores sets the time.  The chunk halves while the grid holds fewer than 512
+// workgroups, down to 256 blocks, then while it holds fewer than 256, down to
+// 32.  Measured on one 32,768-token sequence, (12,1) heads (us, before -> after
+// the second step): 16 rows 22.7 -> 15.3, 64 rows 28.1 -> 21.1, 128 rows
+// 29.0 -> 24.2, 512 rows 47.3 -> 42.6; one target of 256 workgroups for every
+// row count made 2,048 rows slower (94 -> 110), one of 512 with 32-block
+// chunks made 128-256 rows slower (31 -> 40 at 256).
 //
 // When the workgroup's rows belong to one sequence (the usual extend chunk), its
 // waves share each 16-block tile of keys: the threads load it together, it is
@@ -39,8 +45,10 @@ namespace qsa {
 // dims 64 kq + m of row c (A) and of block c (B).  Rows of one wave that belong
 // to different sequences are scored in separate passes.
 constexpr int kTiledChunk = 1024;  // blocks per workgroup (at most)
-constexpr int kTiledMinChunk = 128;
-constexpr int kTiledMinGrid = 512;  // workgroups below which the chunk shrinks
+constexpr int kTiledMidChunk = 256;  // the chunk's floor while the grid is below kTiledMinGrid
+constexpr int kTiledMinGrid = 512;
+constexpr int kTiledMinChunk = 32;   // the chunk's floor while the grid is below kTiledFewGrid
+constexpr int kTiledFewGrid = 256;
 constexpr int kTiledWaves = 4;  // waves (16 query rows each) per workgroup (8: slower)
 constexpr int kSRow = kHeadDim + 8;  // padded key row of an LDS tile plane (bf16 elements)
 // pages of one sequence that a chunk's blocks can span (4-token pages: one per block)
@@ -339,8 +347,10 @@ hipError_t launch_scores_tiled(const PagedKV& kv, const Rows& rows, float* score
                                hipStream_t st) {
     if (rows.R == 0) return hipSuccess;
     const int64_t row_tiles = (rows.R + 16 * kTiledWaves - 1) / (16 * kTiledWaves);
+    auto grid_of = [&](int ch) { return row_tiles * kv.Hkv * ((score_stride + ch - 1) / ch); };
     int chunk = kTiledChunk;
-    while (chunk > kTiledMinChunk && row_tiles * kv.Hkv * ((score_stride + chunk - 1) / chunk) < kTiledMinGrid) chunk /= 2;
+    while (chunk > kTiledMidChunk && grid_of(chunk) < kTiledMinGrid) chunk /= 2;
+    while (chunk > kTiledMinChunk && grid_of(chunk) < kTiledFewGrid) chunk /= 2;
     dim3 grid((unsigned)row_tiles, kv.Hkv, (score_stride + chunk - 1) / chunk);
 #define QSA_TILED(KT)                                                                                            \
     hipLaunchKernelGGL((scores_tiled_kernel<KT, kTiledWaves>), grid, dim3(64 * kTiledWaves), 0, st, rows.q,       \
