@@ -169,6 +169,8 @@ int attn_final(const qsa::PagedKV& p, const qsa::Rows& rows, const int32_t* sel_
     }
     if (out_row_stride != (int64_t)Hq * QSA_HEAD_DIM || !aligned(out, 8))
         return fail(QSA_ERR_UNSUPPORTED, "a split attention writes a dense, 8-byte aligned out");
+    if ((int64_t)R * Hq > 0x7fffffff)  // the merge indexes its rows with 32-bit integers
+        return fail(QSA_ERR_UNSUPPORTED, "%d rows x %d heads exceed 2^31 - 1 merged rows", R, Hq);
     const size_t need = qsa_decode_workspace_bytes(R, Hq, S);
     if (use_scratch) {
         if (need > kScratchBytes)

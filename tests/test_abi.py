@@ -252,6 +252,9 @@ def test_extend_split_rejects():
     assert call(os=Hq * 256 + 8) == qsa.QSA_ERR_UNSUPPORTED         # a split read writes dense rows
     assert call(S=0, ws=None) == qsa.QSA_ERR_INVALID_ARG            # 20 (row, KV head) units: the library splits
     assert "workspace" in qsa.qsa_last_error()
+    big = 1 << 27                                                   # 2^27 rows x 16 heads: 2^31 merged rows
+    assert call(R=big, S=2, wb=1 << 62) == qsa.QSA_ERR_UNSUPPORTED
+    assert "merged rows" in qsa.qsa_last_error()
     dv = kv(v=None)
     assert f(ctypes.byref(dv), *base[1:]) == qsa.QSA_ERR_INVALID_ARG
     # sizes: none for one split or bad arguments; num_splits = 0 covers any split count the library picks
