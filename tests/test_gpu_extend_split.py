@@ -8,7 +8,7 @@ extend call within the same tolerance (only the order of the sums differs).
 Cases: the random extend shapes (several sequences per launch, head pairs down to
 (3,1), page sizes 4-256, k 1-512, bf16 and fp8 caches) at split counts 0 (the
 library's choice), 2, 3, 5, 16 and 64; a small chunk on a long context (the shape
-the split read is for); rows that see nothing; strided query rows; the pipeline's
+the split read is for); the largest k (2,048) at 16 and 64 splits; rows that see nothing; strided query rows; the pipeline's
 extend step."""
 import numpy as np
 import pytest
@@ -96,6 +96,26 @@ def test_extend_split_small_chunk_on_long_context(kv_dtype):
     out, lse = to_np(out), to_np(lse)
     check_decode_against_oracle(case, d, sc, to_np(sel), to_np(cnt), out, lse, case.topk)
     agree_with_unsplit(d, sel, cnt, case.topk, out, lse, f"small chunk {kv_dtype}")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("S", [0, 64])
+def test_extend_split_largest_k(S, kv_dtype):
+    """k = 2,048 (8,192 selected tokens per row) on rows of a 40,000-token sequence and
+    of a short one in one launch, shuffled 64-token pages, (16,2) heads: the library's
+    split count (16) and 64 splits of 32 blocks."""
+    lens = [40000, 700]
+    q_seq = [0] * 9 + [1] * 4
+    q_pos = [39999, 39998, 39000, 30001, 20000, 12345, 8191, 8192, 100] + [699, 698, 300, 3]
+    case = synth.make_case(f"xsplit-k2048-{S}-{kv_dtype}", 625 + S, 16, 2, lens, page_size=64, q_seq=q_seq,
+                           q_pos=q_pos, topk=2048, kv_dtype=kv_dtype)
+    log(f"extend split k=2048 S={S} cache={kv_dtype}")
+    d, sc, sel, cnt = select(case, 2048)
+    out, lse = split_attn(d, sel, cnt, 2048, S)
+    torch.cuda.synchronize()
+    out, lse = to_np(out), to_np(lse)
+    check_decode_against_oracle(case, d, sc, to_np(sel), to_np(cnt), out, lse, 2048)
+    agree_with_unsplit(d, sel, cnt, 2048, out, lse, f"k=2048 S={S} {kv_dtype}")
 
 
 def test_extend_split_rows_that_see_nothing():
