@@ -155,8 +155,8 @@ int scratch_for_current_device(void** ptr) {
 // `workspace`, or with use_scratch to the static scratch (the no-allocation
 // entry point; workspace is then ignored).
 int attn_final(const qsa::PagedKV& p, const qsa::Rows& rows, const int32_t* sel_idx, const int32_t* sel_cnt,
-                 int32_t k, float sc, int32_t num_splits, void* out, int64_t out_row_stride, float* lse,
-                 void* workspace, size_t workspace_bytes, bool use_scratch, hipStream_t st, const char* what) {
+               int32_t k, float sc, int32_t num_splits, void* out, int64_t out_row_stride, float* lse,
+               void* workspace, size_t workspace_bytes, bool use_scratch, hipStream_t st, const char* what) {
     const int Hq = rows.Hq;
     if (!out) return fail(QSA_ERR_INVALID_ARG, "out is NULL");
     if (out_row_stride < (int64_t)Hq * QSA_HEAD_DIM)
@@ -331,7 +331,7 @@ int qsa_sparse_attn_decode(const qsa_kv_t* kv, const void* q, int64_t q_row_stri
                           "qsa_sparse_attn_decode");
     }
     return attn_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, workspace,
-                        workspace_bytes, false, st, "qsa_sparse_attn_decode");
+                      workspace_bytes, false, st, "qsa_sparse_attn_decode");
 }
 
 int qsa_sparse_attn_decode_noalloc(const qsa_kv_t* kv, const void* q, int64_t q_row_stride, int32_t Hq,
@@ -350,7 +350,7 @@ int qsa_sparse_attn_decode_noalloc(const qsa_kv_t* kv, const void* q, int64_t q_
     const float sc = scale > 0.f ? scale : 0.0625f;
     qsa::Rows rows{static_cast<const uint16_t*>(q), q_row_stride, nullptr, nullptr, p.batch, Hq};
     return attn_final(p, rows, sel_idx, sel_cnt, k, sc, num_splits, out, out_row_stride, lse, nullptr, 0, true,
-                        static_cast<hipStream_t>(stream), "qsa_sparse_attn_decode_noalloc");
+                      static_cast<hipStream_t>(stream), "qsa_sparse_attn_decode_noalloc");
 }
 
 size_t qsa_decode_fused_workspace_bytes(const qsa_kv_t* kv, int32_t Hq, int32_t k, int32_t num_splits) {
