@@ -205,11 +205,32 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
     if (!(scale <= FLT_MAX)) scale = FLT_MAX;
     // monotonic in x; the -inf padding lands in bin 0 below every real score
     auto bin_of = [&](float x) { return (int)fminf(fmaxf((x - mn) * scale, 0.f), (float)(kBins - 1)); };
+    // With at most 16 scores per thread, all in registers, each score's bin and
+    // order key are computed once and kept (32 registers) rather than recomputed
+    // by every pass that tests them.
+    constexpr bool CACHE = KL == 0 && KPT <= 16;
+    int bn[CACHE ? KPT : 1];
+    uint32_t ky[CACHE ? KPT : 1];
+    if constexpr (CACHE) {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            bn[e] = bin_of(V(e));
+            ky[e] = order_key(V(e));
+        }
+    }
+    auto BIN = [&](int e) -> int {
+        if constexpr (CACHE) return bn[CACHE ? e : 0];
+        else return bin_of(V(e));
+    };
+    auto KEY = [&](int e) -> uint32_t {
+        if constexpr (CACHE) return ky[CACHE ? e : 0];
+        else return order_key(V(e));
+    };
 
     // ---- pass 1: uniform bins over [mn, mx]
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
-        if (V(e) != -INFINITY) atomicAdd(&hist[bin_of(V(e))], 1);
+        if (V(e) != -INFINITY) atomicAdd(&hist[BIN(e)], 1);
     __syncthreads();
     // the thread whose bins hold the k-th largest names the bin (bins descend with
     // the score from the top one down)
@@ -247,7 +268,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
         // ---- rank the bin's candidates directly
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            if (V(e) != -INFINITY && bin_of(V(e)) == B) {
+            if (V(e) != -INFINITY && BIN(e) == B) {
                 const int slot = atomicAdd(&sh_ncand, 1);
                 cand_val[slot] = V(e);
                 cand_idx[slot] = i0 + e;
@@ -282,8 +303,8 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
-                const uint32_t key = order_key(V(e));
-                if (V(e) != -INFINITY && bin_of(V(e)) == B && (key & mask) == prefix)
+                const uint32_t key = KEY(e);
+                if (V(e) != -INFINITY && BIN(e) == B && (key & mask) == prefix)
                     atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
             }
             __syncthreads();
@@ -308,7 +329,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
     int gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-        const uint32_t key = order_key(V(e));
+        const uint32_t key = KEY(e);
         const bool real = V(e) != -INFINITY;
         gt += real && key > T;
         eq += real && key == T;
@@ -317,7 +338,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         if (V(e) == -INFINITY) continue;
-        const uint32_t key = order_key(V(e));
+        const uint32_t key = KEY(e);
         if (key > T) {
             emit(gt + min(eq, need_eq), i0 + e, V(e));
             ++gt;
