@@ -92,11 +92,14 @@ struct SplitWs {
 // NT threads per row, KPT scores per thread: the first KR in registers, the rest
 // in LDS (a 65,536-block row would not fit 1024 threads x 128 registers).  Thread
 // t owns histogram bins [BPT t, BPT t + BPT).
+// Many-row launches (NT = 512) ask for 8 waves per SIMD (at most 64 registers), so
+// that 4 of their 8-wave workgroups share a CU instead of 3: the 7,810-row prefill
+// (32 scores per thread, a few registers spilled) 508 -> 391-402 us, rows of
+// 4,096 blocks 40.2 -> 36.4 us, C4 58.4 -> 57.6 us, selections bit-equal.
 template <int NT, int KPT, int KR, int MODE>
-__global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ scores, int score_stride,
-                                                      const int32_t* __restrict__ q_pos, int Hkv, int k,
-                                                      int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
-                                                      SplitWs ws) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 8 : 1, 8))) void topk_reg_kernel(
+    const float* __restrict__ scores, int score_stride, const int32_t* __restrict__ q_pos, int Hkv, int k,
+    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt, SplitWs ws) {
     constexpr int NW = NT / 64;
     constexpr int BPT = kBins / NT;
     __shared__ int hist[kBins];
@@ -207,8 +210,9 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
     auto bin_of = [&](float x) { return (int)fminf(fmaxf((x - mn) * scale, 0.f), (float)(kBins - 1)); };
     // With at most 16 scores per thread, all in registers, each score's bin and
     // order key are computed once and kept (32 registers) rather than recomputed
-    // by every pass that tests them.
-    constexpr bool CACHE = KL == 0 && KPT <= 16;
+    // by every pass that tests them; within the 64 registers of a many-row launch,
+    // only up to 8 scores per thread (16 would spill).
+    constexpr bool CACHE = KL == 0 && KPT <= (NT == 512 ? 8 : 16);
     int bn[CACHE ? KPT : 1];
     uint32_t ky[CACHE ? KPT : 1];
     if constexpr (CACHE) {
