@@ -8,8 +8,8 @@ extend call within the same tolerance (only the order of the sums differs).
 Cases: the random extend shapes (several sequences per launch, head pairs down to
 (3,1), page sizes 4-256, k 1-512, bf16 and fp8 caches) at split counts 0 (the
 library's choice), 2, 3, 5, 16 and 64; a small chunk on a long context (the shape
-the split read is for); the largest k (2,048) at 16 and 64 splits; rows that see nothing; strided query rows; the pipeline's
-extend step."""
+the split read is for); the largest k (2,048) at 16 and 64 splits; rows that see
+nothing; strided query rows; the pipeline's extend step."""
 import numpy as np
 import pytest
 import torch
