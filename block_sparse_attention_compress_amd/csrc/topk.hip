@@ -78,6 +78,7 @@ __device__ __forceinline__ int eligible(const int32_t* q_pos, int row, int score
 
 constexpr int kRegThreads = 1024;  // threads per row, unless many rows share the launch
 constexpr int kManyThreads = 512;  // threads per row when rows are many (extend chunks)
+constexpr int kManyThreadsShort = 256;  // ... and at most 16 x 256 = 4,096 blocks long
 constexpr int kBins = 2048;
 
 // Candidate workspace of the two-stage select for long rows: per (row, KV head),
@@ -92,12 +93,13 @@ struct SplitWs {
 // NT threads per row, KPT scores per thread: the first KR in registers, the rest
 // in LDS (a 65,536-block row would not fit 1024 threads x 128 registers).  Thread
 // t owns histogram bins [BPT t, BPT t + BPT).
-// Many-row launches (NT = 512) ask for 8 waves per SIMD (at most 64 registers), so
-// that 4 of their 8-wave workgroups share a CU instead of 3: the 7,810-row prefill
+// Many-row launches (NT = 512 or 256) ask for 8 waves per SIMD (at most 64
+// registers), so that 4 of their 8-wave workgroups (8 of the 4-wave ones) share a
+// CU instead of 3: the 7,810-row prefill
 // (32 scores per thread, a few registers spilled) 508 -> 391-402 us, rows of
 // 4,096 blocks 40.2 -> 36.4 us, C4 58.4 -> 57.6 us, selections bit-equal.
 template <int NT, int KPT, int KR, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 8 : 1, 8))) void topk_reg_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT <= 512 ? 8 : 1, 8))) void topk_reg_kernel(
     const float* __restrict__ scores, int score_stride, const int32_t* __restrict__ q_pos, int Hkv, int k,
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt, SplitWs ws) {
     constexpr int NW = NT / 64;
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 
     // order key are computed once and kept (32 registers) rather than recomputed
     // by every pass that tests them; within the 64 registers of a many-row launch,
     // only up to 8 scores per thread (16 would spill).
-    constexpr bool CACHE = KL == 0 && KPT <= (NT == 512 ? 8 : 16);
+    constexpr bool CACHE = KL == 0 && KPT <= (NT <= 512 ? 8 : 16);
     int bn[CACHE ? KPT : 1];
     uint32_t ky[CACHE ? KPT : 1];
     if constexpr (CACHE) {
@@ -471,8 +473,11 @@ static void launch_reg(int per, dim3 grid, const float* scores, int score_stride
 }
 
 // With many rows per launch (an extend chunk), 512-thread workgroups let several
-// rows share a CU and hide each other's latency (256 and 128 threads were slower);
-// with few rows, 1024 threads shorten each row.
+// rows share a CU and hide each other's latency (256 and 128 threads were slower
+// on rows of 8,192 blocks and more); rows of at most 4,096 blocks take 256 threads,
+// 8 rows to a CU (4,096 rows of 1,024 blocks 24.0 -> 16.0 us, 2,048 rows of 4,096
+// blocks 37.1 -> 32.7 us; selections bit-equal).  With few rows, 1024 threads
+// shorten each row.
 constexpr int kManyRows = 1024;
 
 hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_pos, int R, int Hkv, int k,
@@ -481,7 +486,10 @@ hipError_t launch_topk(const float* scores, int score_stride, const int32_t* q_p
     const int units = R * Hkv;
     const int per = (score_stride + kRegThreads - 1) / kRegThreads;  // scores per thread
     const int per_many = (score_stride + kManyThreads - 1) / kManyThreads;
-    if (units >= kManyRows && per_many <= 64)
+    if (units >= kManyRows && score_stride <= 16 * kManyThreadsShort)
+        launch_reg<0, kManyThreadsShort>((score_stride + kManyThreadsShort - 1) / kManyThreadsShort, dim3(units),
+                                         scores, score_stride, q_pos, Hkv, k, sel_idx, sel_cnt, SplitWs{}, st);
+    else if (units >= kManyRows && per_many <= 64)
         launch_reg<0, kManyThreads>(per_many, dim3(units), scores, score_stride, q_pos, Hkv, k, sel_idx, sel_cnt,
                                     SplitWs{}, st);
     else if (per <= 64)
